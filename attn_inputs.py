@@ -21,6 +21,9 @@ tensor_id Q=0, K=1, V=2, dO=3.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
+
 import numpy as np
 
 GOLDEN = np.uint64(0x9E3779B97F4A7C15)
@@ -63,24 +66,32 @@ def splitmix64(seed: int, start: int, count: int) -> np.ndarray:
         return _mix64(state)
 
 
-def normal_f32(seed: int, n: int, chunk: int = 1 << 23) -> np.ndarray:
-    """``n`` N(0,1) draws as float32 (Box-Muller over SplitMix64 pairs)."""
+def _normal_pairs(seed: int, p0: int, p1: int, out: np.ndarray, n: int) -> None:
+    raw = splitmix64(seed, 2 * p0, 2 * (p1 - p0)).reshape(-1, 2)
+    u = ((raw >> np.uint64(11)).astype(np.float64) + 1.0) * (2.0 ** -53)
+    r = np.sqrt(-2.0 * np.log(u[:, 0]))
+    t = (2.0 * np.pi) * u[:, 1]
+    pair = np.empty((p1 - p0, 2), dtype=np.float64)
+    pair[:, 0] = r * np.cos(t)
+    pair[:, 1] = r * np.sin(t)
+    e0, e1 = 2 * p0, min(n, 2 * p1)
+    out[e0:e1] = pair.reshape(-1)[: e1 - e0].astype(np.float32)
+
+
+def normal_f32(seed: int, n: int, chunk: int = 1 << 21) -> np.ndarray:
+    """``n`` N(0,1) draws as float32 (Box-Muller over SplitMix64 pairs).
+    Chunks are independent slices of the same stream, filled by a thread
+    pool (numpy releases the GIL); the result does not depend on ``chunk``."""
     out = np.empty(n, dtype=np.float32)
     npairs = (n + 1) // 2
-    two_pi = 2.0 * np.pi
-    for p0 in range(0, npairs, chunk):
-        p1 = min(npairs, p0 + chunk)
-        raw = splitmix64(seed, 2 * p0, 2 * (p1 - p0)).reshape(-1, 2)
-        u = ((raw >> np.uint64(11)).astype(np.float64) + 1.0) * (2.0 ** -53)
-        r = np.sqrt(-2.0 * np.log(u[:, 0]))
-        t = two_pi * u[:, 1]
-        pair = np.empty((p1 - p0, 2), dtype=np.float64)
-        pair[:, 0] = r * np.cos(t)
-        pair[:, 1] = r * np.sin(t)
-        flat = pair.reshape(-1)
-        e0 = 2 * p0
-        e1 = min(n, 2 * p1)
-        out[e0:e1] = flat[: e1 - e0].astype(np.float32)
+    spans = [(p0, min(npairs, p0 + chunk)) for p0 in range(0, npairs, chunk)]
+    if len(spans) <= 1:
+        for p0, p1 in spans:
+            _normal_pairs(seed, p0, p1, out, n)
+        return out
+    workers = min(len(spans), os.cpu_count() or 1, 16)
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(lambda sp: _normal_pairs(seed, sp[0], sp[1], out, n), spans))
     return out
 
 

@@ -1,0 +1,215 @@
+"""Throughput of the fused exact-attention path on one MI355X.
+
+One step = the whole hot path over the long-context workload (B=1, H=16,
+S=32768, d=128, bf16): forward + backward without mask, then forward +
+backward with the causal mask.  FLOPs are counted the usual way for
+attention: forward 4*B*H*S^2*d, backward 2.5x that, both halved under the
+causal mask.  Inputs are seeded synthetic N(0,1) draws already resident in
+HBM before the timed region.
+
+Prints ONE JSON line (rank 0) with the step throughput, the per-part
+figures, the roofline of the dominant kernel (its time measured with HIP
+events on the launch stream inside the timed region) and the CPU oracle
+timed on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOPS fwd/bwd, bf16 d=128 S=32k causal+noncausal; % MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak (published)
+WORKLOAD = "long_b1_h16_s32768"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_main_noncausal_long_s32768_traffic.json")
+KERNEL_SOURCES = ["fa_common.h", "fa_bwd.hip"]
+
+
+def flops(B, H, S, d, causal, bwd):
+    f = 4.0 * B * H * S * S * d
+    if bwd:
+        f *= 2.5
+    return f / 2 if causal else f
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "exact_attention_39_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_bytes():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None if absent or taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != kernel_source_hash():
+        return None
+    return float(t["bytes_per_launch"])
+
+
+def cpu_baseline(bits, S, d, scale, rows_n=2048):
+    """The oracle as it stands on `rows_n` query rows of one head (non-causal):
+    forward rows plus the dQ rows of the backward."""
+    import numpy as np
+
+    import attn_inputs as gen
+    import oracle
+
+    threads = min(os.cpu_count() or 1, 16)
+    Q, K, V, dO = (gen.bf16_bits_to_f64(bits[t][0, 0]) for t in ("q", "k", "v", "do"))
+    rows = np.linspace(0, S - 1, rows_n).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.forward_rows(Q, K, V, rows, scale, False, nthreads=threads)
+    oracle.backward_dq_rows(Q, K, V, dO, rows, scale, False, nthreads=threads)
+    dt = time.perf_counter() - t0
+    counted = rows_n * (4.0 + 10.0) * S * d
+    return {"value": counted / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+            "sample": f"{rows_n} query rows of head 0, non-causal S={S} d={d}: oracle forward_rows + "
+                      f"backward_dq_rows, {dt:.1f} s; credited (4+10)*S*d FLOP per row like the GPU step "
+                      f"(the dQ-rows routine does 8*S*d of the 10*S*d, so the CPU figure is flattered)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=24576)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this build measures one MI355X "
+              "(each head is independent; the multi-GPU sharding is described, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import attn_inputs as gen
+    import exact_attention_39_amd as fa
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    fa.load_library()
+    fa.fa_set_softmax_options(8.0, 0, 3)
+    w = gen.WORKLOADS[WORKLOAD]
+    B, H, S, d = w["B"], w["H"], w["S"], w["d"]
+    scale = gen.default_scale(d)
+    print(f"[bench] generating inputs {WORKLOAD} B={B} H={H} S={S} d={d}", file=sys.stderr, flush=True)
+    bits = gen.workload_inputs(WORKLOAD, ("q", "k", "v", "do"))
+
+    def dev(b):
+        return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda()
+
+    q, k, v, do = (dev(bits[t]) for t in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+    dq = torch.empty((B, H, S, d), dtype=torch.float32, device="cuda")
+    dk, dv = torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, S, d) // 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    parts = [("fwd", False), ("bwd_pre", False), ("bwd_main", False),
+             ("fwd", True), ("bwd_pre", True), ("bwd_main", True)]
+
+    def launch(kind, causal):
+        if kind == "fwd":
+            fa.fa_fwd(q, k, v, o, lse, scale, causal, stream)
+        elif kind == "bwd_pre":
+            fa.fa_bwd_preprocess(o, do, dq, ws, stream)
+        else:
+            fa.fa_bwd_main(q, k, v, lse, do, dq, dk, dv, scale, causal, ws, stream)
+
+    def step(events=None):
+        for i, (kind, causal) in enumerate(parts):
+            if events is not None:
+                events[i].record(stream)
+            launch(kind, causal)
+        if events is not None:
+            events[len(parts)].record(stream)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+
+    part_ms = [float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
+               for i in range(len(parts))]
+    step_flop = sum(flops(B, H, S, d, c, bwd) for c in (False, True) for bwd in (False, True))
+    value = step_flop / (ms_step / 1e3) / 1e12
+
+    detail = {}
+    for causal in (False, True):
+        tag = "causal" if causal else "noncausal"
+        i0 = 0 if not causal else 3
+        f_ms = part_ms[i0]
+        b_ms = part_ms[i0 + 1] + part_ms[i0 + 2]
+        for name, ms, fl in (("fwd", f_ms, flops(B, H, S, d, causal, False)),
+                             ("bwd", b_ms, flops(B, H, S, d, causal, True))):
+            tf = fl / (ms / 1e3) / 1e12
+            detail[f"{name}_{tag}"] = {"ms": round(ms, 4), "tflops": round(tf, 1),
+                                       "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
+        detail[f"bwd_{tag}"]["preprocess_ms"] = round(part_ms[i0 + 1], 4)
+
+    # dominant kernel: the longest of the six launches
+    dom = int(np.argmax(part_ms))
+    kind, causal = parts[dom]
+    kname = {"fwd": "fwd_kernel", "bwd_pre": "bwd_pre_kernel", "bwd_main": "bwd_kernel"}[kind]
+    if kind == "bwd_pre":
+        alg = 2.0 * B * H * S * d * 2 + 4.0 * B * H * S + 4.0 * B * H * S * d  # bytes: O, dO read; D, dQ written
+        roof = {"bound": "hbm", "achieved": alg / (part_ms[dom] / 1e3) / 1e9, "peak": 8000.0, "unit": "GB/s"}
+    else:
+        alg = flops(B, H, S, d, causal, kind == "bwd_main")
+        roof = {"bound": "mfma", "achieved": alg / (part_ms[dom] / 1e3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["achieved"] = round(roof["achieved"], 1)
+    roof["frac"] = round(roof["frac"], 4)
+    roof["kernel"] = f"{kname}<d=128,causal={int(causal)}>"
+    roof["launch_ms"] = round(part_ms[dom], 4)
+    roof["traffic"] = traffic_bytes() if (kind, causal) == ("bwd_main", False) else None
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "TFLOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{WORKLOAD}: fwd+bwd non-causal then fwd+bwd causal",
+                   "B": B, "H": H, "S": S, "d": d, "scale": scale, "global_batch": B, "seq_len": S,
+                   "parallelism": "single GPU"},
+        "pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "parts": detail,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle on a row sample)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(bits, S, d, scale, args.cpu_rows)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

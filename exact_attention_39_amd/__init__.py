@@ -1,0 +1,188 @@
+"""Python binding of libfa.so, the gfx950 fused exact-attention library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI of include/fa.h.  PyTorch supplies device memory and
+the current HIP stream.  There is no fallback: if libfa.so is missing or the
+tensors are not on the GPU, the calls raise.
+
+Low-level functions carry the C names (``fa_fwd``, ``fa_bwd``, ...) and take
+torch tensors; ``forward`` / ``backward`` allocate their outputs.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libfa.so")
+
+FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {status_string(code)}")
+
+
+def load_library():
+    """Load libfa.so (built by exact_attention_39_amd.build).  Raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m exact_attention_39_amd.build` "
+                           "(the attention path has no CPU fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, vp, sz, vp]
+    lib.fa_bwd_preprocess.restype = i
+    lib.fa_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_bwd_main.restype = i
+    lib.fa_set_softmax_options.argtypes = [f, i, i]
+    lib.fa_set_softmax_options.restype = i
+    lib.fa_exp2_poly.argtypes = [vp, vp, ctypes.c_int64, i, vp]
+    lib.fa_exp2_poly.restype = i
+    _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return load_library().fa_status_string(int(code)).decode()
+
+
+def _check(code: int, where: str):
+    if code != FA_OK:
+        raise FaError(code, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check_tensor(t, name, dtype, shape):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU (the attention path has no CPU fallback)")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _dims(q):
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, S, d]")
+    return tuple(int(x) for x in q.shape)
+
+
+# ------------------------------------------------------------------ C names
+def fa_fwd(q, k, v, o, lse, scale: float, causal: bool, stream=None):
+    import torch
+    B, H, S, d = _dims(q)
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _check_tensor(t, nm, torch.bfloat16, (B, H, S, d))
+    _check_tensor(lse, "lse", torch.float32, (B, H, S))
+    _check(load_library().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, S, d,
+                                 float(scale), int(bool(causal)), _stream(stream)), "fa_fwd")
+
+
+def fa_bwd_workspace_bytes(B: int, H: int, S: int, d: int) -> int:
+    return int(load_library().fa_bwd_workspace_bytes(B, H, S, d))
+
+
+def _bwd_checks(q, k, v, o, lse, do, dq, dk, dv):
+    import torch
+    B, H, S, d = _dims(q)
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (do, "do"), (dk, "dk"), (dv, "dv")):
+        _check_tensor(t, nm, torch.bfloat16, (B, H, S, d))
+    if o is not None:
+        _check_tensor(o, "o", torch.bfloat16, (B, H, S, d))
+    _check_tensor(lse, "lse", torch.float32, (B, H, S))
+    _check_tensor(dq, "dq", torch.float32, (B, H, S, d))
+    return B, H, S, d
+
+
+def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, scale: float, causal: bool, workspace, stream=None):
+    B, H, S, d = _bwd_checks(q, k, v, o, lse, do, dq, dk, dv)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load_library().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
+                                 _ptr(dk), _ptr(dv), B, H, S, d, float(scale), int(bool(causal)),
+                                 _ptr(workspace), ws_bytes, _stream(stream)), "fa_bwd")
+
+
+def fa_bwd_preprocess(o, do, dq, workspace, stream=None):
+    import torch
+    B, H, S, d = _dims(o)
+    _check_tensor(o, "o", torch.bfloat16, (B, H, S, d))
+    _check_tensor(do, "do", torch.bfloat16, (B, H, S, d))
+    _check_tensor(dq, "dq", torch.float32, (B, H, S, d))
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load_library().fa_bwd_preprocess(_ptr(o), _ptr(do), _ptr(dq), B, H, S, d, _ptr(workspace),
+                                            ws_bytes, _stream(stream)), "fa_bwd_preprocess")
+
+
+def fa_bwd_main(q, k, v, lse, do, dq, dk, dv, scale: float, causal: bool, workspace, stream=None):
+    B, H, S, d = _bwd_checks(q, k, v, None, lse, do, dq, dk, dv)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load_library().fa_bwd_main(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(do), _ptr(dq),
+                                      _ptr(dk), _ptr(dv), B, H, S, d, float(scale), int(bool(causal)),
+                                      _ptr(workspace), ws_bytes, _stream(stream)), "fa_bwd_main")
+
+
+def fa_set_softmax_options(rescale_tau: float = 8.0, poly_eighths: int = 0, poly_degree: int = 3):
+    _check(load_library().fa_set_softmax_options(float(rescale_tau), int(poly_eighths), int(poly_degree)),
+           "fa_set_softmax_options")
+
+
+def fa_exp2_poly(x, y, degree: int = 3, stream=None):
+    import torch
+    _check_tensor(x, "x", torch.float32, tuple(x.shape))
+    _check_tensor(y, "y", torch.float32, tuple(x.shape))
+    _check(load_library().fa_exp2_poly(_ptr(x), _ptr(y), x.numel(), int(degree), _stream(stream)),
+           "fa_exp2_poly")
+
+
+# ------------------------------------------------------------------ allocating wrappers
+def forward(q, k, v, causal: bool = False, scale: float | None = None, stream=None):
+    """(O bf16 [B,H,S,d], LSE fp32 [B,H,S]) for bf16 q, k, v on the GPU."""
+    import torch
+    B, H, S, d = _dims(q)
+    scale = d ** -0.5 if scale is None else scale
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    fa_fwd(q, k, v, o, lse, scale, causal, stream)
+    return o, lse
+
+
+def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, stream=None):
+    """(dQ fp32, dK bf16, dV bf16) for the O, LSE that ``forward`` returned."""
+    import torch
+    B, H, S, d = _dims(q)
+    scale = d ** -0.5 if scale is None else scale
+    dq = torch.empty((B, H, S, d), dtype=torch.float32, device=q.device)
+    dk = torch.empty_like(q)
+    dv = torch.empty_like(q)
+    ws = torch.empty(max(1, fa_bwd_workspace_bytes(B, H, S, d) // 4), dtype=torch.float32, device=q.device)
+    fa_bwd(q, k, v, o, lse, do, dq, dk, dv, scale, causal, ws, stream)
+    return dq, dk, dv

@@ -1,0 +1,181 @@
+// fa_api.hip -- the C ABI declared in include/fa.h: argument validation,
+// template dispatch and the softmax tuning knobs.  No allocation, no
+// synchronisation; every launch goes on the caller's stream.
+#include <math.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "exp2_poly.h"
+#include "fa.h"
+#include "fa_common.h"
+#include "fa_launch.h"
+
+namespace {
+
+std::atomic<float> g_tau{8.0f};
+std::atomic<int> g_poly_eighths{0};
+std::atomic<int> g_poly_degree{3};
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shared shape/flag checks.  Returns FA_OK when the call is well formed;
+// *empty is set when there is nothing to compute.
+fa_status check_shape(int B, int H, int S, int d, bool *empty) {
+    if (B < 0 || H < 0 || S < 0) return FA_ERR_INVALID;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (S > (1 << 24)) return FA_ERR_INVALID;
+    const int64_t bh = (int64_t)B * (int64_t)H;
+    if (bh > INT32_MAX) return FA_ERR_INVALID;
+    // grid sizes: BH * ceil(S / 64) must fit a 32-bit grid dimension
+    if (bh * (((int64_t)S + 63) / 64) > INT32_MAX) return FA_ERR_INVALID;
+    *empty = (bh == 0 || S == 0);
+    return FA_OK;
+}
+
+bool good_scale(float s) { return isfinite(s) && s > 0.0f; }
+
+fa_status hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+__global__ void exp2_poly_kernel(const float *__restrict__ x, float *__restrict__ y, int64_t n,
+                                 int degree) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) y[i] = degree == 5 ? fa_exp2::exp2_poly<5>(x[i]) : fa_exp2::exp2_poly<3>(x[i]);
+}
+
+}  // namespace
+
+namespace fa {
+hipError_t launch_exp2_poly(const float *x, float *y, int64_t n, int degree, hipStream_t st) {
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(exp2_poly_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, y, n, degree);
+    return hipGetLastError();
+}
+}  // namespace fa
+
+extern "C" {
+
+const char *fa_status_string(fa_status s) {
+    switch (s) {
+        case FA_OK: return "FA_OK";
+        case FA_ERR_INVALID: return "FA_ERR_INVALID: invalid argument";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dimension must be 64 or 128";
+        case FA_ERR_HIP: return "FA_ERR_HIP: kernel launch failed";
+    }
+    return "unknown fa_status";
+}
+
+fa_status fa_set_softmax_options(float rescale_tau, int poly_eighths, int poly_degree) {
+    if (!isfinite(rescale_tau) || rescale_tau < 0.0f || rescale_tau > 64.0f) return FA_ERR_INVALID;
+    if (poly_eighths < 0 || poly_eighths > 2) return FA_ERR_INVALID;
+    if (poly_degree != 3 && poly_degree != 5) return FA_ERR_INVALID;
+    g_tau.store(rescale_tau);
+    g_poly_eighths.store(poly_eighths);
+    g_poly_degree.store(poly_degree);
+    return FA_OK;
+}
+
+fa_status fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE, int B, int H,
+                 int S, int d, float scale, int causal, void *stream) {
+    bool empty = false;
+    fa_status st = check_shape(B, H, S, d, &empty);
+    if (st != FA_OK) return st;
+    if (!good_scale(scale) || (causal != 0 && causal != 1)) return FA_ERR_INVALID;
+    if (empty) return FA_OK;
+    if (!Q || !K || !V || !O || !LSE) return FA_ERR_INVALID;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
+        return FA_ERR_INVALID;
+    fa::FwdArgs a{Q, K, V, O, LSE, B * H, S, d, scale, causal == 1,
+                  g_tau.load(), g_poly_eighths.load(), g_poly_degree.load()};
+    return hip_status(fa::launch_fwd(a, (hipStream_t)stream));
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int S, int d) {
+    (void)d;
+    if (B <= 0 || H <= 0 || S <= 0) return 0;
+    return (size_t)B * (size_t)H * (size_t)S * sizeof(float);
+}
+
+static fa_status check_bwd_common(int B, int H, int S, int d, const void *workspace,
+                                  size_t workspace_bytes, bool *empty) {
+    fa_status st = check_shape(B, H, S, d, empty);
+    if (st != FA_OK) return st;
+    if (*empty) return FA_OK;
+    if (!workspace || !aligned16(workspace)) return FA_ERR_INVALID;
+    if (workspace_bytes < fa_bwd_workspace_bytes(B, H, S, d)) return FA_ERR_INVALID;
+    return FA_OK;
+}
+
+fa_status fa_bwd_preprocess(const void *O, const void *dO, float *dQ, int B, int H, int S, int d,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+    bool empty = false;
+    fa_status st = check_bwd_common(B, H, S, d, workspace, workspace_bytes, &empty);
+    if (st != FA_OK || empty) return st;
+    if (!O || !dO || !dQ || !aligned16(O) || !aligned16(dO) || !aligned16(dQ)) return FA_ERR_INVALID;
+    fa::BwdArgs a{};
+    a.O = O;
+    a.dO = dO;
+    a.dQ = dQ;
+    a.Dvec = (float *)workspace;
+    a.BH = B * H;
+    a.S = S;
+    a.d = d;
+    return hip_status(fa::launch_bwd_preprocess(a, (hipStream_t)stream));
+}
+
+fa_status fa_bwd_main(const void *Q, const void *K, const void *V, const float *LSE, const void *dO,
+                      float *dQ, void *dK, void *dV, int B, int H, int S, int d, float scale,
+                      int causal, const void *workspace, size_t workspace_bytes, void *stream) {
+    bool empty = false;
+    fa_status st = check_bwd_common(B, H, S, d, workspace, workspace_bytes, &empty);
+    if (st != FA_OK) return st;
+    if (!good_scale(scale) || (causal != 0 && causal != 1)) return FA_ERR_INVALID;
+    if (empty) return FA_OK;
+    const void *ptrs[] = {Q, K, V, LSE, dO, dQ, dK, dV};
+    for (const void *p : ptrs)
+        if (!p || !aligned16(p)) return FA_ERR_INVALID;
+    fa::BwdArgs a{};
+    a.Q = Q;
+    a.K = K;
+    a.V = V;
+    a.LSE = LSE;
+    a.dO = dO;
+    a.dQ = dQ;
+    a.dK = dK;
+    a.dV = dV;
+    a.Dvec = (float *)workspace;
+    a.BH = B * H;
+    a.S = S;
+    a.d = d;
+    a.scale = scale;
+    a.causal = causal == 1;
+    return hip_status(fa::launch_bwd_main(a, (hipStream_t)stream));
+}
+
+fa_status fa_bwd(const void *Q, const void *K, const void *V, const void *O, const float *LSE,
+                 const void *dO, float *dQ, void *dK, void *dV, int B, int H, int S, int d,
+                 float scale, int causal, void *workspace, size_t workspace_bytes, void *stream) {
+    bool empty = false;
+    fa_status st = check_bwd_common(B, H, S, d, workspace, workspace_bytes, &empty);
+    if (st != FA_OK) return st;
+    if (!good_scale(scale) || (causal != 0 && causal != 1)) return FA_ERR_INVALID;
+    if (empty) return FA_OK;
+    if (!O || !aligned16(O)) return FA_ERR_INVALID;
+    const void *ptrs[] = {Q, K, V, LSE, dO, dQ, dK, dV};
+    for (const void *p : ptrs)
+        if (!p || !aligned16(p)) return FA_ERR_INVALID;
+    st = fa_bwd_preprocess(O, dO, dQ, B, H, S, d, workspace, workspace_bytes, stream);
+    if (st != FA_OK) return st;
+    return fa_bwd_main(Q, K, V, LSE, dO, dQ, dK, dV, B, H, S, d, scale, causal, workspace,
+                       workspace_bytes, stream);
+}
+
+fa_status fa_exp2_poly(const float *x, float *y, int64_t n, int degree, void *stream) {
+    if (n < 0 || (degree != 3 && degree != 5)) return FA_ERR_INVALID;
+    if (n == 0) return FA_OK;
+    if (!x || !y) return FA_ERR_INVALID;
+    if ((n + 255) / 256 > INT32_MAX) return FA_ERR_INVALID;
+    return hip_status(fa::launch_exp2_poly(x, y, n, degree, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,254 @@
+// fa_fwd.hip -- fused exact attention forward for gfx950.
+//
+// Computes, per (batch, head), O = softmax(scale * Q K^T [+ causal mask]) V
+// and LSE = ln of each row's softmax denominator, in one pass over key/value
+// tiles without forming the S x S matrix (the FlashAttention-4 pages: exact
+// attention, hyper.ai story; tiled pipeline, gist.science technical
+// summary, methodology item 1).
+//
+// Work decomposition
+//   * one workgroup = 4 waves = 128 query rows (32 per wave) of one head;
+//     two workgroups share a CU (256 VGPRs per wave, 64 KB LDS each), so
+//     each SIMD interleaves the MFMA phase of one wave with the softmax of
+//     the other -- the MFMA/softmax overlap the pages call ping-pong,
+//     obtained here from the SIMD's wave arbitration;
+//   * key/value tiles of 64 rows stream through LDS, double buffered: the
+//     global loads of tile j+1 are issued before tile j is computed and land
+//     in the other LDS buffer after it;
+//   * per wave and tile: S^T = K Q^T (16 MFMA 32x32x16), online softmax in
+//     registers, O^T += V^T P^T (16 MFMA).  Keeping the transposed products
+//     puts the query index on the lanes, so row max, row sum and the
+//     rescale factor are per lane; only one v_permlane32_swap per tile
+//     joins the two half-waves that hold the two halves of a row.
+//
+// Softmax (the pages' ideas, adapted):
+//   * log2 domain: t = s * scale * log2(e), P = 2^(t - m_ref);
+//   * conditional rescale: the reference max m_ref only moves when a tile's
+//     row max exceeds it by more than tau; otherwise O and l are left alone
+//     and P may reach 2^tau (gist.science German explainer, section 3: skip
+//     the rescale when the numbers do not grow too large).  The decision is
+//     per row, the multiply is skipped for the whole wave when no row needs
+//     it.  The result does not depend on tau beyond rounding;
+//   * hybrid exp2: POLY eighths of the exponentials (a static subset of the
+//     registers) use the FMA polynomial of exp2_poly.h, the rest v_exp_f32
+//     (technical summary, methodology item 2);
+//   * causal tiles are processed longest first: workgroup ids map to the
+//     last query blocks first (LPT, technical summary, results).
+#include "fa_common.h"
+#include "exp2_poly.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kFwdThreads = 256;
+constexpr int kBr = 128;  // query rows per workgroup
+constexpr int kBc = 64;   // key/value rows per tile
+
+template <int POLY, int DEG>
+__device__ __forceinline__ float exp2_sel(float x, int r) {
+    if constexpr (POLY > 0) {
+        if ((r & 7) < POLY) return fa_exp2::exp2_poly<DEG>(x);
+    }
+    return __builtin_amdgcn_exp2f(x);
+}
+
+template <int D, bool CAUSAL, int POLY, int DEG>
+__global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
+    uint16_t *__restrict__ O, float *__restrict__ LSE, int BH, int S, float c, float tau, int nqb) {
+    constexpr int ROWB = D * 2;        // bytes per row
+    constexpr int NCH = ROWB / 16;     // 16-byte chunks per row
+    constexpr int KS = D / 16;         // k-steps over d
+    constexpr int DB = D / 32;         // 32-wide d blocks of O^T
+    constexpr int TILE = kBc * ROWB;   // bytes of one K or V tile
+    constexpr int CPT = kBc * NCH / kFwdThreads;  // 16-byte chunks per thread per tile
+    static_assert(CPT >= 1, "tile too small for the block");
+
+    __shared__ __attribute__((aligned(16))) char smem_raw[2 * 2 * TILE];
+    fa_lds_char *smem = (fa_lds_char *)smem_raw;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int h = lane >> 5, n = lane & 31;
+
+    const int bh = blockIdx.x % BH;
+    const int qi = blockIdx.x / BH;
+    const int qblk = CAUSAL ? (nqb - 1 - qi) : qi;
+    const int q0 = qblk * kBr;
+    const size_t head = (size_t)bh * (size_t)S * D;
+    const int kv_end = CAUSAL ? min(S, q0 + kBr) : S;
+    const int nkv = (kv_end + kBc - 1) / kBc;
+
+    const int qrow = q0 + 32 * w + n;   // this lane's query row
+    const int wq_lo = q0 + 32 * w;      // first query row of the wave
+
+    // Q^T as the B operand of S^T = K Q^T: lane holds Q[qrow][16ks + 8h .. +7].
+    fa_u32x4 qf[KS];
+    {
+        const uint16_t *qp = Q + head + (size_t)qrow * D + 8 * h;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            fa_u32x4 z = {0u, 0u, 0u, 0u};
+            qf[ks] = qrow < S ? *(const fa_u32x4 *)(qp + 16 * ks) : z;
+        }
+    }
+
+    fa_f32x16 oacc[DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i) oacc[i] = zero16();
+    float m_ref = -1.0e30f;  // finite sentinel: no inf - inf when a row's tile is fully masked
+    float l_sum = 0.0f;
+
+    fa_u32x4 stK[CPT], stV[CPT];
+    auto gload = [&](int j) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int id = tid + kFwdThreads * i;
+            const int row = id / NCH, ch = id % NCH;
+            const int kv = j * kBc + row;
+            fa_u32x4 z = {0u, 0u, 0u, 0u};
+            const size_t off = head + (size_t)kv * D + ch * 8;
+            stK[i] = kv < S ? *(const fa_u32x4 *)(K + off) : z;
+            stV[i] = kv < S ? *(const fa_u32x4 *)(V + off) : z;
+        }
+    };
+    auto lstore = [&](int buf) {
+        fa_lds_char *sK = smem + buf * 2 * TILE;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int id = tid + kFwdThreads * i;
+            const int row = id / NCH, ch = id % NCH;
+            const int off = tile_off<NCH>(row, ch * 16);
+            lds_write16(sK, off, stK[i]);
+            lds_write16(sK + TILE, off, stV[i]);
+        }
+    };
+
+    if (nkv > 0) {
+        gload(0);
+        lstore(0);
+    }
+    __syncthreads();
+
+    for (int j = 0; j < nkv; ++j) {
+        const int buf = j & 1;
+        if (j + 1 < nkv) gload(j + 1);
+        const fa_lds_char *sK = smem + buf * 2 * TILE;
+        const fa_lds_char *sV = sK + TILE;
+        const int kv0 = j * kBc;
+        const bool skip = CAUSAL && (kv0 > wq_lo + 31);  // whole tile above this wave's diagonal
+
+        if (!skip) {
+            // S^T = K Q^T for 64 keys x 32 queries: two 32x32 blocks.
+            fa_f32x16 sacc[2] = {zero16(), zero16()};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb) {
+                    const fa_u32x4 a = lds_read16(sK, tile_off<NCH>(32 * mb + n, (2 * ks + h) * 16));
+                    sacc[mb] = mfma32(a, qf[ks], sacc[mb]);
+                }
+            }
+            const bool need_mask = (CAUSAL && (kv0 + kBc - 1 > wq_lo)) || (kv0 + kBc > S);
+            if (need_mask) {
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int kv = kv0 + 32 * mb + 8 * (r >> 2) + 4 * h + (r & 3);
+                        const bool dead = (CAUSAL && kv > qrow) || kv >= S;
+                        sacc[mb][r] = dead ? -INFINITY : sacc[mb][r];
+                    }
+            }
+            // row max over this lane's 32 keys, then across the two half-waves
+            float mx = sacc[0][0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][r]);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][r]);
+            mx = max_halves(mx);
+            const float m_new = mx * c;
+            const bool need = m_new > m_ref + tau;
+            if (__builtin_amdgcn_ballot_w64(need)) {
+                const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
+                m_ref = need ? m_new : m_ref;
+                l_sum *= alpha;
+#pragma unroll
+                for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
+            }
+            const float nm = -m_ref;
+            // P = 2^(s c - m_ref); pack to bf16 in MFMA k order; partial row sum
+            fa_u32x4 pf[4];
+            float lpart = 0.0f;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    const float p0 = exp2_sel<POLY, DEG>(fmaf(sacc[mb][r], c, nm), r);
+                    const float p1 = exp2_sel<POLY, DEG>(fmaf(sacc[mb][r + 1], c, nm), r + 1);
+                    lpart += p0 + p1;
+                    pf[2 * mb + (r >> 3)][(r & 7) >> 1] = pack_bf16(p0, p1);
+                }
+            }
+            l_sum += lpart;
+            // O^T += V^T P^T, k-step t covers keys 16t .. 16t+15 of the tile in
+            // accumulator order; V^T operand by transposing reads of V rows.
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int rbase = 16 * t + 4 * h;  // = 32 mb + 16 t' + 4h
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const fa_u32x4 a = operand_tr<NCH>(sV, rbase, rbase + 8, 32 * db, lane);
+                    oacc[db] = mfma32(a, pf[t], oacc[db]);
+                }
+            }
+        }
+        if (j + 1 < nkv) lstore(buf ^ 1);
+        __syncthreads();
+    }
+
+    // Epilogue: join the half-row sums, normalise, store O (bf16) and LSE.
+    const float l_tot = sum_halves(l_sum);
+    const float inv = 1.0f / l_tot;
+    if (qrow < S) {
+        uint16_t *op = O + head + (size_t)qrow * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                fa_u32x2 v = {pack_bf16(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
+                              pack_bf16(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+                *(fa_u32x2 *)(op + 32 * db + 8 * g + 4 * h) = v;
+            }
+        if (h == 0) LSE[(size_t)bh * S + qrow] = (m_ref + __log2f(l_tot)) * FA_LN2;
+    }
+}
+
+template <int D, bool CAUSAL, int POLY, int DEG>
+hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t st) {
+    const int nqb = (a.S + kBr - 1) / kBr;
+    const dim3 grid((unsigned)(a.BH * nqb)), block(kFwdThreads);
+    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, POLY, DEG>), grid, block, 0, st,
+                       (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
+                       (uint16_t *)a.O, a.LSE, a.BH, a.S, a.scale * FA_LOG2E, a.tau, nqb);
+    return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_fwd_d(const FwdArgs &a, hipStream_t st) {
+    if (a.poly_eighths == 0) return launch_fwd_t<D, CAUSAL, 0, 3>(a, st);
+    if (a.poly_eighths == 1) return a.poly_degree == 5 ? launch_fwd_t<D, CAUSAL, 1, 5>(a, st)
+                                                       : launch_fwd_t<D, CAUSAL, 1, 3>(a, st);
+    return a.poly_degree == 5 ? launch_fwd_t<D, CAUSAL, 2, 5>(a, st)
+                              : launch_fwd_t<D, CAUSAL, 2, 3>(a, st);
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs &a, hipStream_t st) {
+    if (a.d == 128) return a.causal ? launch_fwd_d<128, true>(a, st) : launch_fwd_d<128, false>(a, st);
+    return a.causal ? launch_fwd_d<64, true>(a, st) : launch_fwd_d<64, false>(a, st);
+}
+
+}  // namespace fa

@@ -1,0 +1,39 @@
+// fa_launch.h -- internal launcher interface between the C ABI (fa_api.hip)
+// and the kernel files.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+    const void *Q, *K, *V;
+    void *O;
+    float *LSE;
+    int BH, S, d;
+    float scale;
+    bool causal;
+    float tau;         // rescale threshold, log2 units
+    int poly_eighths;  // 0, 1 or 2
+    int poly_degree;   // 3 or 5
+};
+
+struct BwdArgs {
+    const void *Q, *K, *V, *O, *dO;
+    const float *LSE;
+    float *dQ;
+    void *dK, *dV;
+    float *Dvec;  // workspace, BH*S floats
+    int BH, S, d;
+    float scale;
+    bool causal;
+};
+
+hipError_t launch_fwd(const FwdArgs &a, hipStream_t st);
+hipError_t launch_bwd_preprocess(const BwdArgs &a, hipStream_t st);
+hipError_t launch_bwd_main(const BwdArgs &a, hipStream_t st);
+hipError_t launch_exp2_poly(const float *x, float *y, int64_t n, int degree, hipStream_t st);
+
+}  // namespace fa

@@ -1,0 +1,140 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) fused exact-attention library.
+ *
+ * What the operations compute.  FlashAttention-4 (hyper.ai news story, one
+ * paragraph; gist.science explainer "FlashAttention-4: Algorithm and Kernel
+ * Pipelining Co-Design for Asymmetric Hardware Scaling", technical summary)
+ * is an exact, faster implementation of the standard attention of a
+ * Transformer.  Per (batch b, head h), with queries, keys and values
+ * Q, K, V in R^{S x d}:
+ *
+ *   forward   S = scale * Q K^T, optional causal mask (key j visible to
+ *             query i iff j <= i), P = row-softmax(S), O = P V,
+ *             LSE_i = ln sum_j exp(S_ij) over the visible j.
+ *   backward  for the loss gradient dO:  D_i = sum_k dO_ik O_ik,
+ *             P recomputed from LSE, dV = P^T dO, dP = dO V^T,
+ *             dS = P o (dP - D), dQ = scale * dS K, dK = scale * dS^T Q.
+ *
+ * The forward never forms S x S: it streams key/value tiles with an online
+ * softmax (running row max and sum, output rescaled only when the running
+ * max grows past a threshold, the "skip the rescale when it is not needed"
+ * idea of the gist.science explainer, section 3 of the German page), and
+ * schedules causal tiles longest-first (the LPT causal scheduler of the
+ * technical summary, "Belangrijkste Resultaten").  The backward recomputes P
+ * tile by tile from the saved LSE and accumulates dQ with global fp32 atomic
+ * adds (technical summary, methodology item 3).
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates nothing and keeps no state between calls.
+ *   - Q, K, V, O, dO, dK, dV: bf16 (raw 16-bit patterns), contiguous
+ *     row-major [B][H][S][d].  LSE and the workspace D: fp32 [B][H][S].
+ *     dQ: fp32 [B][H][S][d].
+ *   - Every pointer must be 16-byte aligned.
+ *   - d must be 64 or 128.  S may be any value >= 0 (ragged tails are
+ *     masked).  B, H >= 0.  B*H*S == 0 is a valid empty call that launches
+ *     nothing.  B*H*S*d must fit in int64; S <= 2^24 and B*H <= 2^31-1.
+ *   - scale must be finite and > 0 (1/sqrt(d) is the usual value).
+ *   - causal must be 0 or 1.
+ *   - stream is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue work and never synchronize; results are ready when the stream
+ *     reaches them.  Argument errors are reported synchronously, before
+ *     anything is enqueued.  A failed launch is reported as FA_ERR_HIP.
+ *     Faults inside a kernel surface at the caller's next synchronization.
+ *   - Calls on different streams are independent; the library is safe to
+ *     call from several threads at once.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_INVALID = 1,     /* null/misaligned pointer, bad size, scale or flag */
+    FA_ERR_UNSUPPORTED = 2, /* head dimension other than 64 or 128 */
+    FA_ERR_HIP = 3          /* the HIP runtime refused a launch */
+} fa_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *fa_status_string(fa_status s);
+
+/*
+ * Forward pass.  Writes O (bf16 [B][H][S][d]) and LSE (fp32 [B][H][S],
+ * natural log of the softmax denominator of each query row).  Q, K, V are
+ * read only.  O and LSE must not overlap the inputs.
+ */
+fa_status fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE,
+                 int B, int H, int S, int d, float scale, int causal, void *stream);
+
+/* Bytes of workspace fa_bwd needs: B*H*S fp32 values (the D vector). */
+size_t fa_bwd_workspace_bytes(int B, int H, int S, int d);
+
+/*
+ * Backward pass for the O and LSE that fa_fwd produced from the same Q, K,
+ * V, scale and causal flag.  Writes dQ (fp32 [B][H][S][d]; the library
+ * zeroes it first and accumulates into it with atomic adds, so the low bits
+ * may differ between runs), dK and dV (bf16 [B][H][S][d]).  workspace must
+ * hold at least fa_bwd_workspace_bytes(B, H, S, d) bytes of device memory;
+ * its contents on entry are ignored and on return are D.
+ * Equivalent to fa_bwd_preprocess followed by fa_bwd_main.
+ */
+fa_status fa_bwd(const void *Q, const void *K, const void *V, const void *O, const float *LSE,
+                 const void *dO, float *dQ, void *dK, void *dV,
+                 int B, int H, int S, int d, float scale, int causal,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * First half of fa_bwd: D_i = sum_k dO_ik O_ik (fp32, into workspace) and
+ * dQ := 0.  Same argument rules as fa_bwd.
+ */
+fa_status fa_bwd_preprocess(const void *O, const void *dO, float *dQ,
+                            int B, int H, int S, int d,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Second half of fa_bwd: recompute P from LSE, accumulate dV, dK and dQ.
+ * Expects the workspace D and the zeroed dQ that fa_bwd_preprocess left on
+ * the same stream.
+ */
+fa_status fa_bwd_main(const void *Q, const void *K, const void *V, const float *LSE,
+                      const void *dO, float *dQ, void *dK, void *dV,
+                      int B, int H, int S, int d, float scale, int causal,
+                      const void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Tuning knobs of the forward softmax, process-wide, read by every later
+ * fa_fwd / fa_bwd call.
+ *   rescale_tau: the running row max (in log2 units) is moved, and O and
+ *     the row sum rescaled, only when a new tile's max exceeds it by more
+ *     than tau.  tau >= 0 and finite; 0 rescales on every increase.  Any
+ *     tau gives the same exact result up to rounding; unnormalised
+ *     probabilities stay below 2^tau.  Default 8.
+ *   poly_eighths: how many eighths (0, 1 or 2) of the exponentials use the
+ *     FMA polynomial exp2 instead of the hardware v_exp_f32 (the hybrid
+ *     split of the technical summary, methodology item 2).  Default 0: on
+ *     gfx950 the hardware exponential costs about two FMA slots, the
+ *     polynomial about seven.
+ *   poly_degree: 3 or 5.
+ * Returns FA_ERR_INVALID for values outside these sets.
+ */
+fa_status fa_set_softmax_options(float rescale_tau, int poly_eighths, int poly_degree);
+
+/*
+ * Diagnostic: y[i] = exp2 of x[i] through the device polynomial of the given
+ * degree (3 or 5), as the forward kernel evaluates it.  x, y: device fp32
+ * arrays of n elements.  For x < -126 the result is 0; the polynomial is
+ * meant for x <= 2^7.
+ */
+fa_status fa_exp2_poly(const float *x, float *y, int64_t n, int degree, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,110 @@
+"""The C-ABI library without a GPU: it loads, exports every function that
+include/fa.h declares, and rejects malformed calls before touching the GPU
+(argument checks run on the host, ahead of any HIP call)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import exact_attention_39_amd as fa
+    if not os.path.exists(fa.LIB_PATH):
+        pytest.fail("libfa.so is not built: run __graft_entry__.build()")
+    return fa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert {"fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string"} <= set(names)
+    nm = subprocess.check_output(["nm", "-D", "--defined-only", os.path.join(ROOT, "exact_attention_39_amd", "libfa.so")],
+                                 text=True)
+    exported = {l.split()[-1] for l in nm.splitlines() if " T " in l}
+    for n in names:
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+
+
+def test_status_strings(lib):
+    for code in range(4):
+        assert lib.fa_status_string(code).decode().startswith("FA_")
+
+
+NULL = None
+A = ctypes.c_void_p(0x10000)   # aligned fake device addresses (never dereferenced: calls fail first)
+MIS = ctypes.c_void_p(0x10008)
+
+
+def fwd(lib, B=1, H=1, S=128, d=128, scale=0.088, causal=0, ptrs=None):
+    p = ptrs or [A, A, A, A, A]
+    return lib.fa_fwd(*p, B, H, S, d, ctypes.c_float(scale), causal, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), 1), (dict(H=-2), 1), (dict(S=-5), 1), (dict(d=96), 2), (dict(d=256), 2),
+    (dict(scale=0.0), 1), (dict(scale=-1.0), 1), (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1),
+    (dict(causal=2), 1), (dict(causal=-1), 1), (dict(S=(1 << 24) + 1), 1),
+])
+def test_forward_rejects_bad_arguments(lib, kw, code):
+    assert fwd(lib, **kw) == code
+
+
+def test_forward_rejects_null_and_misaligned(lib):
+    assert fwd(lib, ptrs=[A, A, A, NULL, A]) == 1
+    assert fwd(lib, ptrs=[A, MIS, A, A, A]) == 1
+    assert fwd(lib, ptrs=[A, A, A, A, MIS]) == 1
+
+
+def test_empty_calls_are_ok_without_gpu(lib):
+    assert fwd(lib, S=0, ptrs=[NULL] * 5) == 0
+    assert fwd(lib, B=0, ptrs=[NULL] * 5) == 0
+    ws = lib.fa_bwd_workspace_bytes(1, 1, 0, 128)
+    assert ws == 0
+    assert lib.fa_bwd(*([NULL] * 9), 1, 1, 0, 128, ctypes.c_float(0.1), 1, NULL, 0, NULL) == 0
+
+
+def test_backward_checks(lib):
+    assert lib.fa_bwd_workspace_bytes(2, 3, 100, 128) == 2 * 3 * 100 * 4
+    p9 = [A] * 9
+    # workspace too small
+    assert lib.fa_bwd(*p9, 1, 1, 128, 128, ctypes.c_float(0.1), 0, A, 4, NULL) == 1
+    # null workspace
+    assert lib.fa_bwd(*p9, 1, 1, 128, 128, ctypes.c_float(0.1), 0, NULL, 512, NULL) == 1
+    # misaligned dQ
+    p = list(p9)
+    p[6] = MIS
+    assert lib.fa_bwd(*p, 1, 1, 128, 128, ctypes.c_float(0.1), 0, A, 512, NULL) == 1
+    assert lib.fa_bwd(*p9, 1, 1, 128, 64 + 1, ctypes.c_float(0.1), 0, A, 512, NULL) == 2
+    assert lib.fa_bwd_main(*([A] * 8), 1, 1, 128, 128, ctypes.c_float(0.1), 3, A, 512, NULL) == 1
+    assert lib.fa_bwd_preprocess(A, A, MIS, 1, 1, 128, 128, A, 512, NULL) == 1
+
+
+def test_softmax_options_validation(lib):
+    assert lib.fa_set_softmax_options(ctypes.c_float(-1.0), 0, 3) == 1
+    assert lib.fa_set_softmax_options(ctypes.c_float(8.0), 3, 3) == 1
+    assert lib.fa_set_softmax_options(ctypes.c_float(8.0), 1, 4) == 1
+    assert lib.fa_set_softmax_options(ctypes.c_float(float("nan")), 0, 3) == 1
+    assert lib.fa_set_softmax_options(ctypes.c_float(8.0), 0, 3) == 0
+    assert lib.fa_exp2_poly(NULL, NULL, -1, 3, NULL) == 1
+    assert lib.fa_exp2_poly(NULL, NULL, 0, 3, NULL) == 0
+    assert lib.fa_exp2_poly(A, A, 16, 4, NULL) == 1
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    import exact_attention_39_amd as fa
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        fa.forward(q, q, q)

@@ -1,0 +1,273 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU fp64 oracle.
+
+Tolerances (fixed by the attention target, written here once):
+  O     max |O - O_ref| <= 2e-2 and mean |O - O_ref| <= 2e-3
+  LSE   max |LSE - LSE_ref| <= 1e-3
+  dQ, dK, dV   max |g - g_ref| / max |g_ref| <= 5e-2  (per tensor);
+               where g_ref is identically zero, max |g| <= 1e-4
+
+Both sides see the same bf16 inputs from attn_inputs (seeded SplitMix64 +
+Box-Muller, rounded to bf16); the oracle widens them exactly to fp64.
+Small shapes are compared element by element over whole tensors; the
+workload shapes are compared on sampled query rows (O, LSE, dQ) and sampled
+key rows (dK, dV) that the oracle computes one by one.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import attn_inputs as gen
+import oracle
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+O_MAX, O_MEAN, LSE_MAX, G_REL = 2e-2, 2e-3, 1e-3, 5e-2
+G_ABS_ZERO = 1e-4  # for gradients that are exactly zero
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def fa():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the -m gpu tests need an MI355X")
+    import exact_attention_39_amd as m
+    m.load_library()
+    m.fa_set_softmax_options(8.0, 0, 3)
+    return m
+
+
+def to_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def bf16_to_np64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def rand_bits(shape, seed, scale=1.0):
+    x = gen.normal_f32(seed, int(np.prod(shape))).reshape(shape) * np.float32(scale)
+    return gen.f32_to_bf16_bits(x)
+
+
+def check_o(o, ref, what):
+    err = np.abs(o - ref)
+    assert err.max() <= O_MAX and err.mean() <= O_MEAN, f"{what}: O max {err.max():.3e} mean {err.mean():.3e}"
+
+
+def check_lse(l, ref, what):
+    err = np.abs(l - ref).max()
+    assert err <= LSE_MAX, f"{what}: LSE max err {err:.3e}"
+
+
+def check_grad(g, ref, what):
+    peak = np.abs(ref).max()
+    if peak == 0.0:
+        # degenerate case (e.g. S = 1: one key, so dS = 0 and dQ = dK = 0
+        # exactly); the relative form is undefined, bound the rounding noise
+        # absolutely instead.
+        assert np.abs(g).max() <= G_ABS_ZERO, f"{what}: max |g| {np.abs(g).max():.3e} for a zero gradient"
+        return 0.0
+    rel = np.abs(g - ref).max() / peak
+    assert rel <= G_REL, f"{what}: rel err {rel:.3e}"
+    return rel
+
+
+def run_fwd(fa, qb, kb, vb, causal, scale):
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    o, lse = fa.forward(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return q, k, v, o, lse
+
+
+# ------------------------------------------------------------------ whole tensors, small shapes
+SMALL = [
+    # (B, H, S, d, causal)  -- several tiles and ragged tails
+    (1, 2, 256, 64, False),
+    (1, 2, 256, 64, True),
+    (2, 3, 300, 128, False),
+    (2, 3, 300, 128, True),
+    (1, 1, 1, 128, False),
+    (1, 1, 1, 64, True),
+    (1, 2, 130, 64, True),
+    (1, 1, 129, 128, True),
+    (1, 2, 64, 128, False),
+    (1, 1, 515, 128, True),
+    (1, 1, 200, 64, False),
+]
+
+
+@pytest.mark.parametrize("B,H,S,d,causal", SMALL)
+def test_small_forward_backward_full_tensors(fa, B, H, S, d, causal):
+    say(f"[small] B={B} H={H} S={S} d={d} causal={causal}")
+    shape = (B, H, S, d)
+    seed = 1000 + S * 7 + d + int(causal)
+    qb, kb, vb, db = (rand_bits(shape, seed + i) for i in range(4))
+    scale = 1.0 / np.sqrt(d)
+    q, k, v, o, lse = run_fwd(fa, qb, kb, vb, causal, scale)
+    Q, K, V, dO = (gen.bf16_bits_to_f64(x) for x in (qb, kb, vb, db))
+    o_ref, lse_ref = oracle.attention_forward(Q, K, V, scale, causal)
+    check_o(bf16_to_np64(o), o_ref, "fwd")
+    check_lse(lse.cpu().numpy().astype(np.float64), lse_ref, "fwd")
+    do = to_dev(db)
+    dq, dk, dv = fa.backward(q, k, v, o, lse, do, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    gq, gk, gv = oracle.attention_backward(Q, K, V, dO, scale, causal)
+    check_grad(dq.cpu().numpy().astype(np.float64), gq, "dQ")
+    check_grad(bf16_to_np64(dk), gk, "dK")
+    check_grad(bf16_to_np64(dv), gv, "dV")
+
+
+def test_smoke_workload_forward(fa):
+    """fp32 host draws -> bf16 device, B=1 H=2 S=256 d=64, non-causal, all elements."""
+    name = "smoke_d64_s256"
+    say(f"[workload] {name}")
+    w = gen.WORKLOADS[name]
+    bits = gen.workload_inputs(name, ("q", "k", "v"))
+    scale = gen.default_scale(w["d"])
+    _, _, _, o, lse = run_fwd(fa, bits["q"], bits["k"], bits["v"], False, scale)
+    Q, K, V = (gen.bf16_bits_to_f64(bits[t]) for t in "qkv")
+    o_ref, lse_ref = oracle.attention_forward(Q, K, V, scale, False)
+    check_o(bf16_to_np64(o), o_ref, name)
+    check_lse(lse.cpu().numpy().astype(np.float64), lse_ref, name)
+
+
+def test_empty_inputs_launch_nothing(fa):
+    say("[edge] empty inputs")
+    for shape in [(1, 1, 0, 128), (0, 4, 64, 64), (2, 0, 64, 128)]:
+        q = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
+        o, lse = fa.forward(q, q, q, causal=True)
+        dq, dk, dv = fa.backward(q, q, q, o, lse, q, causal=True)
+        torch.cuda.synchronize()
+        assert o.shape == shape and lse.shape == shape[:3] and dq.shape == shape
+
+
+def test_forward_repeatable_and_rescale_options_agree(fa):
+    say("[ab] tau / poly options")
+    B, H, S, d = 1, 4, 1024, 128
+    shape = (B, H, S, d)
+    qb = rand_bits(shape, 77, scale=3.0)  # large scores: the running max moves often
+    kb, vb = rand_bits(shape, 78), rand_bits(shape, 79)
+    scale = 1.0 / np.sqrt(d)
+    Q, K, V = (gen.bf16_bits_to_f64(x) for x in (qb, kb, vb))
+    refs = {c: oracle.attention_forward(Q, K, V, scale, c) for c in (False, True)}
+    try:
+        for tau, poly, deg in [(8.0, 0, 3), (0.0, 0, 3), (8.0, 1, 3), (8.0, 2, 3), (8.0, 2, 5), (2.0, 1, 5)]:
+            fa.fa_set_softmax_options(tau, poly, deg)
+            for causal in (False, True):
+                _, _, _, o, lse = run_fwd(fa, qb, kb, vb, causal, scale)
+                what = f"tau={tau} poly={poly}/8 deg={deg} causal={causal}"
+                check_o(bf16_to_np64(o), refs[causal][0], what)
+                check_lse(lse.cpu().numpy().astype(np.float64), refs[causal][1], what)
+                _, _, _, o2, lse2 = run_fwd(fa, qb, kb, vb, causal, scale)
+                assert torch.equal(o, o2) and torch.equal(lse, lse2), f"{what}: not repeatable"
+    finally:
+        fa.fa_set_softmax_options(8.0, 0, 3)
+
+
+def test_device_exp2_polynomial(fa):
+    say("[exp2] device polynomial")
+    x = np.concatenate([np.linspace(-126.0, 0.0, 1 << 20), np.linspace(0.0, 8.0, 1 << 16),
+                        np.arange(-126, 9, dtype=np.float64)]).astype(np.float32)
+    xd = torch.from_numpy(x).cuda()
+    for deg in (3, 5):
+        y = torch.empty_like(xd)
+        fa.fa_exp2_poly(xd, y, deg)
+        torch.cuda.synchronize()
+        ref = np.exp2(x.astype(np.float64))
+        rel = np.abs(y.cpu().numpy().astype(np.float64) / ref - 1.0).max()
+        assert rel <= 2e-4, (deg, rel)
+    low = torch.tensor([-np.inf, -127.0, -200.0], dtype=torch.float32, device="cuda")
+    y = torch.empty_like(low)
+    fa.fa_exp2_poly(low, y, 3)
+    torch.cuda.synchronize()
+    assert torch.all(y == 0)
+
+
+# ------------------------------------------------------------------ workload shapes, sampled
+def sample_rows(S, extra=()):
+    rng = np.random.default_rng(S)
+    base = {0, 1, 31, 32, 63, 64, 127, 128, 129, S // 2, S - 129, S - 128, S - 65, S - 64, S - 2, S - 1}
+    base |= set(int(x) for x in rng.integers(0, S, 24))
+    base |= set(extra)
+    return np.array(sorted(r for r in base if 0 <= r < S), dtype=np.int64)
+
+
+_WORKLOAD_CACHE = {}
+
+
+def workload_bits(name):
+    """All four tensors of a workload, generated once per test session."""
+    if name not in _WORKLOAD_CACHE:
+        _WORKLOAD_CACHE.clear()  # keep one workload resident at a time
+        _WORKLOAD_CACHE[name] = gen.workload_inputs(name, ("q", "k", "v", "do"))
+    return _WORKLOAD_CACHE[name]
+
+
+def head_f64(bits, b, h):
+    return gen.bf16_bits_to_f64(bits[b, h])
+
+
+WORKLOAD_FWD = [
+    ("fwd_b4_h16_s4096", False),
+    ("causal_boost_b2_h16_s8192", True),
+    ("causal_fwdbwd_b2_h16_s16384", True),
+    ("long_b1_h16_s32768", False),
+    ("long_b1_h16_s32768", True),
+]
+
+
+@pytest.mark.parametrize("name,causal", WORKLOAD_FWD)
+def test_workload_forward_sampled(fa, name, causal):
+    say(f"[workload fwd] {name} causal={causal}")
+    w = gen.WORKLOADS[name]
+    bits = workload_bits(name)
+    scale = gen.default_scale(w["d"])
+    _, _, _, o, lse = run_fwd(fa, bits["q"], bits["k"], bits["v"], causal, scale)
+    S = w["S"]
+    boosted = range(0, S, 64) if w["boost"] else ()
+    rows = sample_rows(S, extra=list(boosted)[:: max(1, len(boosted) // 16)] if boosted else ())
+    heads = [(0, 0), (w["B"] - 1, w["H"] - 1)]
+    for b, h in heads:
+        Q, K, V = (head_f64(bits[t], b, h) for t in "qkv")
+        o_ref, l_ref = oracle.forward_rows(Q, K, V, rows, scale, causal)
+        o_g = bf16_to_np64(o[b, h, torch.from_numpy(rows).cuda()])
+        l_g = lse[b, h, torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+        check_o(o_g, o_ref, f"{name} head ({b},{h})")
+        check_lse(l_g, l_ref, f"{name} head ({b},{h})")
+
+
+WORKLOAD_BWD = [
+    ("causal_fwdbwd_b2_h16_s16384", True),
+    ("long_b1_h16_s32768", False),
+    ("long_b1_h16_s32768", True),
+]
+
+
+@pytest.mark.parametrize("name,causal", WORKLOAD_BWD)
+def test_workload_backward_sampled(fa, name, causal):
+    say(f"[workload bwd] {name} causal={causal}")
+    w = gen.WORKLOADS[name]
+    bits = workload_bits(name)
+    scale = gen.default_scale(w["d"])
+    q, k, v, o, lse = run_fwd(fa, bits["q"], bits["k"], bits["v"], causal, scale)
+    do = to_dev(bits["do"])
+    dq, dk, dv = fa.backward(q, k, v, o, lse, do, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    S = w["S"]
+    b, h = w["B"] - 1, w["H"] - 1
+    Q, K, V, dO = (head_f64(bits[t], b, h) for t in ("q", "k", "v", "do"))
+    rows = sample_rows(S)
+    gq = oracle.backward_dq_rows(Q, K, V, dO, rows, scale, causal)
+    idx = torch.from_numpy(rows).cuda()
+    check_grad(dq[b, h, idx].cpu().numpy().astype(np.float64), gq, f"{name} dQ rows")
+    cols = np.array(sorted({0, 1, 127, 128, S // 3, S // 2, S - 129, S - 128, S - 1}), dtype=np.int64)
+    gk, gv = oracle.backward_dkdv_cols(Q, K, V, dO, cols, scale, causal)
+    cidx = torch.from_numpy(cols).cuda()
+    check_grad(bf16_to_np64(dk[b, h, cidx]), gk, f"{name} dK cols")
+    check_grad(bf16_to_np64(dv[b, h, cidx]), gv, f"{name} dV cols")

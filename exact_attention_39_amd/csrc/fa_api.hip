@@ -24,7 +24,7 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 fa_status check_shape(int B, int H, int S, int d, bool *empty) {
     if (B < 0 || H < 0 || S < 0) return FA_ERR_INVALID;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-    if (S > (1 << 24)) return FA_ERR_INVALID;
+    if (S > (1 << 22)) return FA_ERR_INVALID;  // per-head byte offsets stay 32-bit
     const int64_t bh = (int64_t)B * (int64_t)H;
     if (bh > INT32_MAX) return FA_ERR_INVALID;
     // grid sizes: BH * ceil(S / 64) must fit a 32-bit grid dimension

@@ -14,7 +14,8 @@
 //     it keeps its K and V rows resident (as MFMA B operands in registers,
 //     and K once more in LDS for the dQ product) and its dK, dV
 //     accumulators in registers, and streams query blocks of 64 rows;
-//   * per query block: Q, dO (double-buffered in LDS), LSE, D; per wave
+//   * per query block: Q, dO, LSE, D copied straight from memory into a
+//     double-buffered LDS stage (buffer_load ... lds); per wave
 //     S = Q K^T and dP = dO V^T (keys on the lanes), P and dS in registers,
 //     dV += P^T dO and dK += dS^T Q with P, dS straight from the
 //     accumulators and dO, Q through transposing LDS reads; dS^T goes to
@@ -76,19 +77,16 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
     constexpr int QTILE = kQPerIter * ROWB;
     constexpr int KTILE = kKvPerBlock * ROWB;
     constexpr int DSTILE = kKvPerBlock * kQPerIter * 2;  // dS^T: 128 key rows x 64 queries
-    constexpr int CPTQ = kQPerIter * NCH / kBwdThreads;
-    constexpr int CPTK = kKvPerBlock * NCH / kBwdThreads;
-    static_assert(CPTQ >= 1 && CPTK >= 1, "tile too small for the block");
 
-    __shared__ __attribute__((aligned(16))) char smem_raw[KTILE + 4 * QTILE + DSTILE + 4 * kQPerIter * 4];
+    __shared__ __attribute__((aligned(1024))) char smem_raw[KTILE + 4 * QTILE + DSTILE + 4 * kQPerIter * 4];
     fa_lds_char *smem = (fa_lds_char *)smem_raw;
     fa_lds_char *sK = smem;
     fa_lds_char *sQ0 = smem + KTILE;             // [2] Q tiles
     fa_lds_char *sO0 = sQ0 + 2 * QTILE;          // [2] dO tiles
     fa_lds_char *sdS = sO0 + 2 * QTILE;          // dS^T tile
-    fa_lds_char *sLD = sdS + DSTILE;             // [2][LSE2 64 | D 64] floats
+    fa_lds_char *sLD = sdS + DSTILE;             // [2][LSE 64 | D 64] floats
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int h = lane >> 5, n = lane & 31;
 
     const int bh = blockIdx.x % BH;
@@ -97,25 +95,26 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
     const size_t head = (size_t)bh * (size_t)S * D;
     const int kv = k0 + 32 * w + n;  // this lane's key for S and dP
 
-    // Resident B operands: K[kv][16ks + 8h ..] and V[kv][..].
+    // Per-head buffer resources (rows at or past S read as zero, are never written).
+    const uint32_t head_bytes = (uint32_t)S * ROWB;
+    const fa_rsrc rQ = make_rsrc(Q + head, head_bytes);
+    const fa_rsrc rK = make_rsrc(K + head, head_bytes);
+    const fa_rsrc rV = make_rsrc(V + head, head_bytes);
+    const fa_rsrc rdO = make_rsrc(dO + head, head_bytes);
+    const fa_rsrc rL = make_rsrc(LSE + (size_t)bh * S, (uint32_t)S * 4);
+    const fa_rsrc rD = make_rsrc(Dvec + (size_t)bh * S, (uint32_t)S * 4);
+    const fa_rsrc rdQ = make_rsrc(dQ + head, (uint32_t)S * D * 4);
+
+    // Resident B operands: K[kv][16ks + 8h ..] and V[kv][..]; K tile in LDS
+    // for the dQ product.
     fa_u32x4 kf[KS], vf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-        const fa_u32x4 z = {0u, 0u, 0u, 0u};
-        const size_t off = head + (size_t)kv * D + 16 * ks + 8 * h;
-        kf[ks] = kv < S ? *(const fa_u32x4 *)(K + off) : z;
-        vf[ks] = kv < S ? *(const fa_u32x4 *)(V + off) : z;
+        const uint32_t off = (uint32_t)kv * ROWB + (16 * ks + 8 * h) * 2;
+        kf[ks] = buf_load16(rK, off);
+        vf[ks] = buf_load16(rV, off);
     }
-    // K tile in LDS for the dQ product.
-#pragma unroll
-    for (int i = 0; i < CPTK; ++i) {
-        const int id = tid + kBwdThreads * i;
-        const int row = id / NCH, ch = id % NCH;
-        const int kr = k0 + row;
-        const fa_u32x4 z = {0u, 0u, 0u, 0u};
-        const fa_u32x4 v = kr < S ? *(const fa_u32x4 *)(K + head + (size_t)kr * D + ch * 8) : z;
-        lds_write16(sK, tile_off<NCH>(row, ch * 16), v);
-    }
+    tile_to_lds<NCH, kKvPerBlock>(rK, k0, sK, w, lane);
 
     fa_f32x16 dkacc[DB], dvacc[DB];
 #pragma unroll
@@ -127,52 +126,25 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
     const int nqb = (S + kQPerIter - 1) / kQPerIter;
     const int ib = CAUSAL ? k0 / kQPerIter : 0;
 
-    fa_u32x4 stQ[CPTQ], stO[CPTQ];
-    float stLD = 0.0f;
-    auto gload = [&](int i) {
-        const int q0 = i * kQPerIter;
-#pragma unroll
-        for (int cc = 0; cc < CPTQ; ++cc) {
-            const int id = tid + kBwdThreads * cc;
-            const int row = id / NCH, ch = id % NCH;
-            const int q = q0 + row;
-            const fa_u32x4 z = {0u, 0u, 0u, 0u};
-            const size_t off = head + (size_t)q * D + ch * 8;
-            stQ[cc] = q < S ? *(const fa_u32x4 *)(Q + off) : z;
-            stO[cc] = q < S ? *(const fa_u32x4 *)(dO + off) : z;
+    // Query block i -> LDS buffer: Q and dO tiles (all waves), LSE (wave 0)
+    // and D (wave 1).  Rows past S arrive as zeros; such rows then carry
+    // dO = 0 and D = 0, so they add nothing to dV, dK or dS.
+    auto issue = [&](int i, int buf) {
+        tile_to_lds<NCH, kQPerIter>(rQ, i * kQPerIter, sQ0 + buf * QTILE, w, lane);
+        tile_to_lds<NCH, kQPerIter>(rdO, i * kQPerIter, sO0 + buf * QTILE, w, lane);
+        if (w < 2) {
+            fa_lds_char *dst = sLD + (buf * 2 + w) * kQPerIter * 4;
+            buf_load_lds<4>(w == 0 ? rL : rD, dst, (uint32_t)(i * kQPerIter + lane) * 4);
         }
-        if (tid < kQPerIter) {
-            const int q = q0 + tid;
-            stLD = q < S ? LSE[(size_t)bh * S + q] * FA_LOG2E : INFINITY;
-        } else if (tid < 2 * kQPerIter) {
-            const int q = q0 + tid - kQPerIter;
-            stLD = q < S ? Dvec[(size_t)bh * S + q] : 0.0f;
-        }
-    };
-    auto lstore = [&](int buf) {
-        fa_lds_char *tq = sQ0 + buf * QTILE;
-        fa_lds_char *to = sO0 + buf * QTILE;
-#pragma unroll
-        for (int cc = 0; cc < CPTQ; ++cc) {
-            const int id = tid + kBwdThreads * cc;
-            const int row = id / NCH, ch = id % NCH;
-            const int off = tile_off<NCH>(row, ch * 16);
-            lds_write16(tq, off, stQ[cc]);
-            lds_write16(to, off, stO[cc]);
-        }
-        if (tid < 2 * kQPerIter)
-            *(__attribute__((address_space(3))) float *)(sLD + (buf * 2 * kQPerIter + tid) * 4) = stLD;
     };
 
-    if (ib < nqb) {
-        gload(ib);
-        lstore(0);
-    }
+    if (ib < nqb) issue(ib, 0);
+    wait_vmem();
     __syncthreads();
 
     for (int i = ib; i < nqb; ++i) {
         const int buf = (i - ib) & 1;
-        if (i + 1 < nqb) gload(i + 1);
+        if (i + 1 < nqb) issue(i + 1, buf ^ 1);
         const int q0 = i * kQPerIter;
         const fa_lds_char *sQ = sQ0 + buf * QTILE;
         const fa_lds_char *sO = sO0 + buf * QTILE;
@@ -206,7 +178,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * g + e;
-                    float pv = __builtin_amdgcn_exp2f(fmaf(sacc[qb][r], c, -l4[e]));
+                    float pv = __builtin_amdgcn_exp2f(fmaf(sacc[qb][r], c, -l4[e] * FA_LOG2E));
                     if (need_mask) {
                         const int q = q0 + qi + e;
                         const bool dead = (CAUSAL && kv > q) || kv >= S;
@@ -243,28 +215,35 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
         // dQ slice of this wave: d = 128 -> (d block w, both query blocks);
         // d = 64 -> (query block w/2, d block w%2).  Keys in natural order.
         constexpr int NQB = (DB == 4) ? 2 : 1;
+        fa_f32x16 dqacc[NQB];
 #pragma unroll
         for (int u = 0; u < NQB; ++u) {
             const int qb = (DB == 4) ? u : (w >> 1);
             const int db = (DB == 4) ? w : (w & 1);
-            fa_f32x16 acc = zero16();
+            dqacc[u] = zero16();
 #pragma unroll
             for (int ks = 0; ks < kKvPerBlock / 16; ++ks) {
                 const int r0 = 16 * ks + 8 * h;
                 const fa_u32x4 a = operand_tr<8>(sdS, r0, r0 + 4, 32 * qb, lane);
                 const fa_u32x4 b = operand_tr<NCH>(sK, r0, r0 + 4, 32 * db, lane);
-                acc = mfma32(a, b, acc);
+                dqacc[u] = mfma32(a, b, dqacc[u]);
             }
-            float *dqp = dQ + head + (size_t)(q0 + 32 * qb) * D + 32 * db + n;
+        }
+        wait_vmem();      // next query block landed (and older dQ atomics retired)
+        __syncthreads();  // ... for every wave; dS^T and this block's tiles are free
+
+        // dQ += partial, fp32 atomics; rows past S fall outside the resource.
+#pragma unroll
+        for (int u = 0; u < NQB; ++u) {
+            const int qb = (DB == 4) ? u : (w >> 1);
+            const int db = (DB == 4) ? w : (w & 1);
+            const uint32_t base = ((uint32_t)(q0 + 32 * qb) * D + 32 * db + n) * 4;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int qr = 8 * (r >> 2) + 4 * h + (r & 3);
-                if (q0 + 32 * qb + qr < S) unsafeAtomicAdd(dqp + (size_t)qr * D, acc[r]);
+                buf_atomic_add(rdQ, base + (uint32_t)qr * D * 4, dqacc[u][r]);
             }
         }
-
-        if (i + 1 < nqb) lstore(buf ^ 1);
-        __syncthreads();
     }
 
     // Epilogue: dK, dV rows of this workgroup (lane = d column, registers = keys).
@@ -273,11 +252,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int kr = k0 + 32 * w + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (kr < S) {
-                const size_t off = head + (size_t)kr * D + 32 * db + n;
-                dK[off] = (uint16_t)(pack_bf16(dkacc[db][r], 0.0f) & 0xFFFFu);
-                dV[off] = (uint16_t)(pack_bf16(dvacc[db][r], 0.0f) & 0xFFFFu);
-            }
+            const uint32_t off = ((uint32_t)kr * D + 32 * db + n) * 2;
+            buf_store2(make_rsrc(dK + head, head_bytes), off, (uint16_t)(pack_bf16(dkacc[db][r], 0.0f) & 0xFFFFu));
+            buf_store2(make_rsrc(dV + head, head_bytes), off, (uint16_t)(pack_bf16(dvacc[db][r], 0.0f) & 0xFFFFu));
         }
     }
 }

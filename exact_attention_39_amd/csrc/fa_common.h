@@ -37,6 +37,7 @@ typedef float fa_f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t fa_u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t fa_u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) char fa_lds_char;
+typedef __amdgpu_buffer_rsrc_t fa_rsrc;
 
 #define FA_LOG2E 1.4426950408889634f
 #define FA_LN2 0.6931471805599453f
@@ -61,6 +62,53 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// Raw buffer resources.  A buffer access whose byte offset lies at or past
+// num_records is dropped by the hardware (loads return 0, stores and atomics
+// do nothing), which replaces per-row bounds branches for ragged tails.
+__device__ __forceinline__ fa_rsrc make_rsrc(const void *base, uint32_t num_bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)num_bytes, 0x00020000);
+}
+
+__device__ __forceinline__ fa_u32x4 buf_load16(fa_rsrc r, uint32_t off) {
+    return __builtin_bit_cast(fa_u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ void buf_store8(fa_rsrc r, uint32_t off, fa_u32x2 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(fa_u32x2, v), r, off, 0, 0);
+}
+
+__device__ __forceinline__ void buf_store4(fa_rsrc r, uint32_t off, uint32_t v) {
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
+}
+
+__device__ __forceinline__ void buf_store2(fa_rsrc r, uint32_t off, uint16_t v) {
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
+}
+
+__device__ __forceinline__ void buf_atomic_add(fa_rsrc r, uint32_t off, float v) {
+    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, off, 0, 0);
+}
+
+// Direct global -> LDS copy (buffer_load ... lds): every lane of the wave
+// fetches BYTES (4 or 16) at its own byte offset and the hardware stores them
+// at lds_wave_base + lane * BYTES.  lds_wave_base must be wave-uniform.
+template <int BYTES>
+__device__ __forceinline__ void buf_load_lds(fa_rsrc r, fa_lds_char *lds_wave_base, uint32_t off) {
+    auto *dst = (__attribute__((address_space(3))) void *)lds_wave_base;
+    if constexpr (BYTES == 16) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, off, 0, 0, 0);
+    } else {
+        static_assert(BYTES == 4, "4- or 16-byte lanes");
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, off, 0, 0, 0);
+    }
+}
+
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+// Wait until every outstanding vector-memory operation of this wave is done.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 
@@ -73,6 +121,29 @@ __device__ __forceinline__ int swz(int row) {
     } else {
         static_assert(NCH == 8, "rows of 128 or 256 bytes");
         return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+    }
+}
+
+// Copy ROWS rows of a row-major global matrix (row pitch NCH*16 bytes,
+// starting at byte offset row0 * pitch of the resource) into a swizzled LDS
+// tile with 4 waves (w = wave index, wave-uniform), straight from memory to LDS.  Each wave instruction
+// fills 1 KB of LDS contiguously, so the swizzle is applied on the global
+// side: the lane that owns physical chunk pc of a row fetches logical chunk
+// pc ^ swz(row).  Rows past the resource end arrive as zeros.
+template <int NCH, int ROWS>
+__device__ __forceinline__ void tile_to_lds(fa_rsrc r, int row0, fa_lds_char *tile, int w, int lane) {
+    constexpr int ROWB = NCH * 16;
+    constexpr int ROWS_PER_INST = 1024 / ROWB;
+    constexpr int INSTS = ROWS * ROWB / 1024;   // wave instructions for the tile
+    static_assert(INSTS % 4 == 0, "tile must split evenly over 4 waves");
+#pragma unroll
+    for (int k = 0; k < INSTS / 4; ++k) {
+        const int inst = w + 4 * k;
+        const int row = inst * ROWS_PER_INST + lane / NCH;
+        const int pc = lane % NCH;
+        const int c = pc ^ swz<NCH>(row);
+        const uint32_t goff = (uint32_t)(row0 + row) * ROWB + c * 16;
+        buf_load_lds<16>(r, tile + inst * 1024, goff);
     }
 }
 

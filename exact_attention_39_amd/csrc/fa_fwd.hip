@@ -13,8 +13,8 @@
 //     the other -- the MFMA/softmax overlap the pages call ping-pong,
 //     obtained here from the SIMD's wave arbitration;
 //   * key/value tiles of 64 rows stream through LDS, double buffered: the
-//     global loads of tile j+1 are issued before tile j is computed and land
-//     in the other LDS buffer after it;
+//     direct memory-to-LDS copies of tile j+1 (buffer_load ... lds) are
+//     issued before tile j is computed and land in the other buffer;
 //   * per wave and tile: S^T = K Q^T (16 MFMA 32x32x16), online softmax in
 //     registers, O^T += V^T P^T (16 MFMA).  Keeping the transposed products
 //     puts the query index on the lanes, so row max, row sum and the
@@ -63,13 +63,11 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(
     constexpr int KS = D / 16;         // k-steps over d
     constexpr int DB = D / 32;         // 32-wide d blocks of O^T
     constexpr int TILE = kBc * ROWB;   // bytes of one K or V tile
-    constexpr int CPT = kBc * NCH / kFwdThreads;  // 16-byte chunks per thread per tile
-    static_assert(CPT >= 1, "tile too small for the block");
 
-    __shared__ __attribute__((aligned(16))) char smem_raw[2 * 2 * TILE];
+    __shared__ __attribute__((aligned(1024))) char smem_raw[2 * 2 * TILE];
     fa_lds_char *smem = (fa_lds_char *)smem_raw;
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int h = lane >> 5, n = lane & 31;
 
     const int bh = blockIdx.x % BH;
@@ -83,16 +81,17 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(
     const int qrow = q0 + 32 * w + n;   // this lane's query row
     const int wq_lo = q0 + 32 * w;      // first query row of the wave
 
+    // Per-head buffer resources: rows at or past S read as zero and are
+    // never written.
+    const uint32_t head_bytes = (uint32_t)S * ROWB;
+    const fa_rsrc rQ = make_rsrc(Q + head, head_bytes);
+    const fa_rsrc rK = make_rsrc(K + head, head_bytes);
+    const fa_rsrc rV = make_rsrc(V + head, head_bytes);
+
     // Q^T as the B operand of S^T = K Q^T: lane holds Q[qrow][16ks + 8h .. +7].
     fa_u32x4 qf[KS];
-    {
-        const uint16_t *qp = Q + head + (size_t)qrow * D + 8 * h;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            fa_u32x4 z = {0u, 0u, 0u, 0u};
-            qf[ks] = qrow < S ? *(const fa_u32x4 *)(qp + 16 * ks) : z;
-        }
-    }
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = buf_load16(rQ, (uint32_t)qrow * ROWB + (16 * ks + 8 * h) * 2);
 
     fa_f32x16 oacc[DB];
 #pragma unroll
@@ -100,40 +99,19 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(
     float m_ref = -1.0e30f;  // finite sentinel: no inf - inf when a row's tile is fully masked
     float l_sum = 0.0f;
 
-    fa_u32x4 stK[CPT], stV[CPT];
-    auto gload = [&](int j) {
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int id = tid + kFwdThreads * i;
-            const int row = id / NCH, ch = id % NCH;
-            const int kv = j * kBc + row;
-            fa_u32x4 z = {0u, 0u, 0u, 0u};
-            const size_t off = head + (size_t)kv * D + ch * 8;
-            stK[i] = kv < S ? *(const fa_u32x4 *)(K + off) : z;
-            stV[i] = kv < S ? *(const fa_u32x4 *)(V + off) : z;
-        }
-    };
-    auto lstore = [&](int buf) {
+    auto issue_tile = [&](int j, int buf) {
         fa_lds_char *sK = smem + buf * 2 * TILE;
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int id = tid + kFwdThreads * i;
-            const int row = id / NCH, ch = id % NCH;
-            const int off = tile_off<NCH>(row, ch * 16);
-            lds_write16(sK, off, stK[i]);
-            lds_write16(sK + TILE, off, stV[i]);
-        }
+        tile_to_lds<NCH, kBc>(rK, j * kBc, sK, w, lane);
+        tile_to_lds<NCH, kBc>(rV, j * kBc, sK + TILE, w, lane);
     };
 
-    if (nkv > 0) {
-        gload(0);
-        lstore(0);
-    }
+    if (nkv > 0) issue_tile(0, 0);
+    wait_vmem();
     __syncthreads();
 
     for (int j = 0; j < nkv; ++j) {
         const int buf = j & 1;
-        if (j + 1 < nkv) gload(j + 1);
+        if (j + 1 < nkv) issue_tile(j + 1, buf ^ 1);
         const fa_lds_char *sK = smem + buf * 2 * TILE;
         const fa_lds_char *sV = sK + TILE;
         const int kv0 = j * kBc;
@@ -204,24 +182,25 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(
                 }
             }
         }
-        if (j + 1 < nkv) lstore(buf ^ 1);
-        __syncthreads();
+        wait_vmem();      // tile j+1 has landed in the other buffer
+        __syncthreads();  // ... for every wave, and nobody still reads this one
     }
 
     // Epilogue: join the half-row sums, normalise, store O (bf16) and LSE.
     const float l_tot = sum_halves(l_sum);
     const float inv = 1.0f / l_tot;
-    if (qrow < S) {
-        uint16_t *op = O + head + (size_t)qrow * D;
+    const fa_rsrc rO = make_rsrc(O + head, head_bytes);
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                fa_u32x2 v = {pack_bf16(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
-                              pack_bf16(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
-                *(fa_u32x2 *)(op + 32 * db + 8 * g + 4 * h) = v;
-            }
-        if (h == 0) LSE[(size_t)bh * S + qrow] = (m_ref + __log2f(l_tot)) * FA_LN2;
+        for (int g = 0; g < 4; ++g) {
+            fa_u32x2 v = {pack_bf16(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
+                          pack_bf16(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+            buf_store8(rO, (uint32_t)qrow * ROWB + (32 * db + 8 * g + 4 * h) * 2, v);
+        }
+    if (h == 0) {
+        const fa_rsrc rL = make_rsrc(LSE + (size_t)bh * S, (uint32_t)S * 4);
+        buf_store4(rL, (uint32_t)qrow * 4, __float_as_uint((m_ref + __log2f(l_tot)) * FA_LN2));
     }
 }
 

@@ -33,7 +33,7 @@
  *   - Every pointer must be 16-byte aligned.
  *   - d must be 64 or 128.  S may be any value >= 0 (ragged tails are
  *     masked).  B, H >= 0.  B*H*S == 0 is a valid empty call that launches
- *     nothing.  B*H*S*d must fit in int64; S <= 2^24 and B*H <= 2^31-1.
+ *     nothing.  S <= 2^22 (per-head offsets are 32-bit) and B*H <= 2^31-1.
  *   - scale must be finite and > 0 (1/sqrt(d) is the usual value).
  *   - causal must be 0 or 1.
  *   - stream is a hipStream_t (NULL = the default stream).  Calls only

@@ -28,8 +28,8 @@ if ROOT not in sys.path:
 METRIC = "attention TFLOPS fwd/bwd, bf16 d=128 S=32k causal+noncausal; % MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak (published)
 WORKLOAD = "long_b1_h16_s32768"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_main_noncausal_long_s32768_traffic.json")
-KERNEL_SOURCES = ["fa_common.h", "fa_bwd.hip"]
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["fa_common.h", "fa_fwd.hip", "fa_bwd.hip"]
 
 
 def flops(B, H, S, d, causal, bwd):
@@ -47,17 +47,19 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def traffic_bytes():
-    """HBM bytes per launch of the dominant kernel from the committed counter
-    summary, or None if absent or taken on different kernel sources."""
+def traffic_bytes(kname, causal):
+    """HBM bytes per launch of a kernel from the committed counter summary
+    (profiles/traffic_long_s32768.json), or None if absent or taken on other
+    kernel sources."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(TRAFFIC_DIR, "traffic_long_s32768.json")) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     if t.get("source_sha256") != kernel_source_hash():
         return None
-    return float(t["bytes_per_launch"])
+    v = t.get("bytes_per_launch", {}).get(f"{kname}{'_causal' if causal else ''}")
+    return None if v is None else float(v)
 
 
 def cpu_baseline(bits, S, d, scale, rows_n=2048):
@@ -121,16 +123,19 @@ def main():
     ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, S, d) // 4, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    parts = [("fwd", False), ("bwd_pre", False), ("bwd_main", False),
-             ("fwd", True), ("bwd_pre", True), ("bwd_main", True)]
+    parts = [("fwd", False), ("bwd_pre", False), ("bwd_dkdv", False), ("bwd_dq", False),
+             ("fwd", True), ("bwd_pre", True), ("bwd_dkdv", True), ("bwd_dq", True)]
+    NP = len(parts) // 2
 
     def launch(kind, causal):
         if kind == "fwd":
             fa.fa_fwd(q, k, v, o, lse, scale, causal, stream)
         elif kind == "bwd_pre":
-            fa.fa_bwd_preprocess(o, do, dq, ws, stream)
+            fa.fa_bwd_preprocess(o, do, ws, stream)
+        elif kind == "bwd_dkdv":
+            fa.fa_bwd_dkdv(q, k, v, lse, do, dk, dv, scale, causal, ws, stream)
         else:
-            fa.fa_bwd_main(q, k, v, lse, do, dq, dk, dv, scale, causal, ws, stream)
+            fa.fa_bwd_dq(q, k, v, lse, do, dq, scale, causal, ws, stream)
 
     def step(events=None):
         for i, (kind, causal) in enumerate(parts):
@@ -163,25 +168,32 @@ def main():
     detail = {}
     for causal in (False, True):
         tag = "causal" if causal else "noncausal"
-        i0 = 0 if not causal else 3
+        i0 = 0 if not causal else NP
         f_ms = part_ms[i0]
-        b_ms = part_ms[i0 + 1] + part_ms[i0 + 2]
+        b_ms = part_ms[i0 + 1] + part_ms[i0 + 2] + part_ms[i0 + 3]
         for name, ms, fl in (("fwd", f_ms, flops(B, H, S, d, causal, False)),
                              ("bwd", b_ms, flops(B, H, S, d, causal, True))):
             tf = fl / (ms / 1e3) / 1e12
             detail[f"{name}_{tag}"] = {"ms": round(ms, 4), "tflops": round(tf, 1),
                                        "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
         detail[f"bwd_{tag}"]["preprocess_ms"] = round(part_ms[i0 + 1], 4)
+        detail[f"bwd_{tag}"]["dkdv_ms"] = round(part_ms[i0 + 2], 4)
+        detail[f"bwd_{tag}"]["dq_ms"] = round(part_ms[i0 + 3], 4)
 
-    # dominant kernel: the longest of the six launches
+    # dominant kernel: the longest launch of the step.  Algorithmic FLOPs per
+    # launch: fwd 4*B*H*S^2*d; dK/dV kernel: S, dP, dV and dK contractions
+    # (8*B*H*S^2*d); dQ kernel: the dQ contraction only (2*B*H*S^2*d) -- its
+    # recomputed S and dP are extra work, not credited.  Halved when causal.
     dom = int(np.argmax(part_ms))
     kind, causal = parts[dom]
-    kname = {"fwd": "fwd_kernel", "bwd_pre": "bwd_pre_kernel", "bwd_main": "bwd_kernel"}[kind]
+    kname = {"fwd": "fwd_kernel", "bwd_pre": "bwd_pre_kernel", "bwd_dkdv": "bwd_dkdv_kernel",
+             "bwd_dq": "bwd_dq_kernel"}[kind]
+    cfac = 0.5 if causal else 1.0
     if kind == "bwd_pre":
-        alg = 2.0 * B * H * S * d * 2 + 4.0 * B * H * S + 4.0 * B * H * S * d  # bytes: O, dO read; D, dQ written
+        alg = 2.0 * B * H * S * d * 2 + 4.0 * B * H * S  # bytes: O, dO read; D written
         roof = {"bound": "hbm", "achieved": alg / (part_ms[dom] / 1e3) / 1e9, "peak": 8000.0, "unit": "GB/s"}
     else:
-        alg = flops(B, H, S, d, causal, kind == "bwd_main")
+        alg = {"fwd": 4.0, "bwd_dkdv": 8.0, "bwd_dq": 2.0}[kind] * B * H * S * S * d * cfac
         roof = {"bound": "mfma", "achieved": alg / (part_ms[dom] / 1e3) / 1e12, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
@@ -189,7 +201,8 @@ def main():
     roof["frac"] = round(roof["frac"], 4)
     roof["kernel"] = f"{kname}<d=128,causal={int(causal)}>"
     roof["launch_ms"] = round(part_ms[dom], 4)
-    roof["traffic"] = traffic_bytes() if (kind, causal) == ("bwd_main", False) else None
+    roof["traffic"] = traffic_bytes(kname, causal)
+    roof["launch_ms_all"] = {f"{k}{'_causal' if c else ''}": round(m, 4) for (k, c), m in zip(parts, part_ms)}
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "TFLOPS", "n_gpus": 1,

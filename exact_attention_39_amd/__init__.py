@@ -45,10 +45,12 @@ def load_library():
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_bwd.restype = i
-    lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, vp, sz, vp]
+    lib.fa_bwd_preprocess.argtypes = [vp, vp, i, i, i, i, vp, sz, vp]
     lib.fa_bwd_preprocess.restype = i
-    lib.fa_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
-    lib.fa_bwd_main.restype = i
+    lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_bwd_dkdv.restype = i
+    lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_bwd_dq.restype = i
     lib.fa_set_softmax_options.argtypes = [f, i, i]
     lib.fa_set_softmax_options.restype = i
     lib.fa_exp2_poly.argtypes = [vp, vp, ctypes.c_int64, i, vp]
@@ -131,23 +133,44 @@ def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, scale: float, causal: bool, workspac
                                  _ptr(workspace), ws_bytes, _stream(stream)), "fa_bwd")
 
 
-def fa_bwd_preprocess(o, do, dq, workspace, stream=None):
+def fa_bwd_preprocess(o, do, workspace, stream=None):
     import torch
     B, H, S, d = _dims(o)
     _check_tensor(o, "o", torch.bfloat16, (B, H, S, d))
     _check_tensor(do, "do", torch.bfloat16, (B, H, S, d))
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load_library().fa_bwd_preprocess(_ptr(o), _ptr(do), B, H, S, d, _ptr(workspace), ws_bytes,
+                                            _stream(stream)), "fa_bwd_preprocess")
+
+
+def _grad_checks(q, k, v, lse, do):
+    import torch
+    B, H, S, d = _dims(q)
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (do, "do")):
+        _check_tensor(t, nm, torch.bfloat16, (B, H, S, d))
+    _check_tensor(lse, "lse", torch.float32, (B, H, S))
+    return B, H, S, d
+
+
+def fa_bwd_dkdv(q, k, v, lse, do, dk, dv, scale: float, causal: bool, workspace, stream=None):
+    import torch
+    B, H, S, d = _grad_checks(q, k, v, lse, do)
+    _check_tensor(dk, "dk", torch.bfloat16, (B, H, S, d))
+    _check_tensor(dv, "dv", torch.bfloat16, (B, H, S, d))
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load_library().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(do), _ptr(dk), _ptr(dv),
+                                      B, H, S, d, float(scale), int(bool(causal)), _ptr(workspace), ws_bytes,
+                                      _stream(stream)), "fa_bwd_dkdv")
+
+
+def fa_bwd_dq(q, k, v, lse, do, dq, scale: float, causal: bool, workspace, stream=None):
+    import torch
+    B, H, S, d = _grad_checks(q, k, v, lse, do)
     _check_tensor(dq, "dq", torch.float32, (B, H, S, d))
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check(load_library().fa_bwd_preprocess(_ptr(o), _ptr(do), _ptr(dq), B, H, S, d, _ptr(workspace),
-                                            ws_bytes, _stream(stream)), "fa_bwd_preprocess")
-
-
-def fa_bwd_main(q, k, v, lse, do, dq, dk, dv, scale: float, causal: bool, workspace, stream=None):
-    B, H, S, d = _bwd_checks(q, k, v, None, lse, do, dq, dk, dv)
-    ws_bytes = workspace.numel() * workspace.element_size()
-    _check(load_library().fa_bwd_main(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(do), _ptr(dq),
-                                      _ptr(dk), _ptr(dv), B, H, S, d, float(scale), int(bool(causal)),
-                                      _ptr(workspace), ws_bytes, _stream(stream)), "fa_bwd_main")
+    _check(load_library().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(do), _ptr(dq), B, H, S, d,
+                                    float(scale), int(bool(causal)), _ptr(workspace), ws_bytes,
+                                    _stream(stream)), "fa_bwd_dq")
 
 
 def fa_set_softmax_options(rescale_tau: float = 8.0, poly_eighths: int = 0, poly_degree: int = 3):

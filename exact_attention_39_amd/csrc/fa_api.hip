@@ -106,16 +106,15 @@ static fa_status check_bwd_common(int B, int H, int S, int d, const void *worksp
     return FA_OK;
 }
 
-fa_status fa_bwd_preprocess(const void *O, const void *dO, float *dQ, int B, int H, int S, int d,
+fa_status fa_bwd_preprocess(const void *O, const void *dO, int B, int H, int S, int d,
                             void *workspace, size_t workspace_bytes, void *stream) {
     bool empty = false;
     fa_status st = check_bwd_common(B, H, S, d, workspace, workspace_bytes, &empty);
     if (st != FA_OK || empty) return st;
-    if (!O || !dO || !dQ || !aligned16(O) || !aligned16(dO) || !aligned16(dQ)) return FA_ERR_INVALID;
+    if (!O || !dO || !aligned16(O) || !aligned16(dO)) return FA_ERR_INVALID;
     fa::BwdArgs a{};
     a.O = O;
     a.dO = dO;
-    a.dQ = dQ;
     a.Dvec = (float *)workspace;
     a.BH = B * H;
     a.S = S;
@@ -123,51 +122,78 @@ fa_status fa_bwd_preprocess(const void *O, const void *dO, float *dQ, int B, int
     return hip_status(fa::launch_bwd_preprocess(a, (hipStream_t)stream));
 }
 
-fa_status fa_bwd_main(const void *Q, const void *K, const void *V, const float *LSE, const void *dO,
-                      float *dQ, void *dK, void *dV, int B, int H, int S, int d, float scale,
-                      int causal, const void *workspace, size_t workspace_bytes, void *stream) {
-    bool empty = false;
-    fa_status st = check_bwd_common(B, H, S, d, workspace, workspace_bytes, &empty);
+// Common checks of the two gradient kernels; fills the launch arguments.
+static fa_status bwd_grad_args(const void *Q, const void *K, const void *V, const float *LSE,
+                               const void *dO, int B, int H, int S, int d, float scale, int causal,
+                               const void *workspace, size_t workspace_bytes, fa::BwdArgs *a,
+                               bool *empty) {
+    fa_status st = check_bwd_common(B, H, S, d, workspace, workspace_bytes, empty);
     if (st != FA_OK) return st;
     if (!good_scale(scale) || (causal != 0 && causal != 1)) return FA_ERR_INVALID;
-    if (empty) return FA_OK;
-    const void *ptrs[] = {Q, K, V, LSE, dO, dQ, dK, dV};
+    if (*empty) return FA_OK;
+    const void *ptrs[] = {Q, K, V, LSE, dO};
     for (const void *p : ptrs)
         if (!p || !aligned16(p)) return FA_ERR_INVALID;
-    fa::BwdArgs a{};
-    a.Q = Q;
-    a.K = K;
-    a.V = V;
-    a.LSE = LSE;
-    a.dO = dO;
-    a.dQ = dQ;
+    *a = fa::BwdArgs{};
+    a->Q = Q;
+    a->K = K;
+    a->V = V;
+    a->LSE = LSE;
+    a->dO = dO;
+    a->Dvec = (float *)workspace;
+    a->BH = B * H;
+    a->S = S;
+    a->d = d;
+    a->scale = scale;
+    a->causal = causal == 1;
+    return FA_OK;
+}
+
+fa_status fa_bwd_dkdv(const void *Q, const void *K, const void *V, const float *LSE, const void *dO,
+                      void *dK, void *dV, int B, int H, int S, int d, float scale, int causal,
+                      const void *workspace, size_t workspace_bytes, void *stream) {
+    fa::BwdArgs a;
+    bool empty = false;
+    fa_status st = bwd_grad_args(Q, K, V, LSE, dO, B, H, S, d, scale, causal, workspace,
+                                 workspace_bytes, &a, &empty);
+    if (st != FA_OK || empty) return st;
+    if (!dK || !dV || !aligned16(dK) || !aligned16(dV)) return FA_ERR_INVALID;
     a.dK = dK;
     a.dV = dV;
-    a.Dvec = (float *)workspace;
-    a.BH = B * H;
-    a.S = S;
-    a.d = d;
-    a.scale = scale;
-    a.causal = causal == 1;
-    return hip_status(fa::launch_bwd_main(a, (hipStream_t)stream));
+    return hip_status(fa::launch_bwd_dkdv(a, (hipStream_t)stream));
+}
+
+fa_status fa_bwd_dq(const void *Q, const void *K, const void *V, const float *LSE, const void *dO,
+                    float *dQ, int B, int H, int S, int d, float scale, int causal,
+                    const void *workspace, size_t workspace_bytes, void *stream) {
+    fa::BwdArgs a;
+    bool empty = false;
+    fa_status st = bwd_grad_args(Q, K, V, LSE, dO, B, H, S, d, scale, causal, workspace,
+                                 workspace_bytes, &a, &empty);
+    if (st != FA_OK || empty) return st;
+    if (!dQ || !aligned16(dQ)) return FA_ERR_INVALID;
+    a.dQ = dQ;
+    return hip_status(fa::launch_bwd_dq(a, (hipStream_t)stream));
 }
 
 fa_status fa_bwd(const void *Q, const void *K, const void *V, const void *O, const float *LSE,
                  const void *dO, float *dQ, void *dK, void *dV, int B, int H, int S, int d,
                  float scale, int causal, void *workspace, size_t workspace_bytes, void *stream) {
+    fa::BwdArgs a;
     bool empty = false;
-    fa_status st = check_bwd_common(B, H, S, d, workspace, workspace_bytes, &empty);
-    if (st != FA_OK) return st;
-    if (!good_scale(scale) || (causal != 0 && causal != 1)) return FA_ERR_INVALID;
-    if (empty) return FA_OK;
-    if (!O || !aligned16(O)) return FA_ERR_INVALID;
-    const void *ptrs[] = {Q, K, V, LSE, dO, dQ, dK, dV};
-    for (const void *p : ptrs)
+    fa_status st = bwd_grad_args(Q, K, V, LSE, dO, B, H, S, d, scale, causal, workspace,
+                                 workspace_bytes, &a, &empty);
+    if (st != FA_OK || empty) return st;
+    const void *outs[] = {O, dQ, dK, dV};
+    for (const void *p : outs)
         if (!p || !aligned16(p)) return FA_ERR_INVALID;
-    st = fa_bwd_preprocess(O, dO, dQ, B, H, S, d, workspace, workspace_bytes, stream);
+    st = fa_bwd_preprocess(O, dO, B, H, S, d, workspace, workspace_bytes, stream);
     if (st != FA_OK) return st;
-    return fa_bwd_main(Q, K, V, LSE, dO, dQ, dK, dV, B, H, S, d, scale, causal, workspace,
-                       workspace_bytes, stream);
+    st = fa_bwd_dkdv(Q, K, V, LSE, dO, dK, dV, B, H, S, d, scale, causal, workspace, workspace_bytes,
+                     stream);
+    if (st != FA_OK) return st;
+    return fa_bwd_dq(Q, K, V, LSE, dO, dQ, B, H, S, d, scale, causal, workspace, workspace_bytes,
+                     stream);
 }
 
 fa_status fa_exp2_poly(const float *x, float *y, int64_t n, int degree, void *stream) {

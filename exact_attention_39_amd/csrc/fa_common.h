@@ -73,6 +73,14 @@ __device__ __forceinline__ fa_u32x4 buf_load16(fa_rsrc r, uint32_t off) {
     return __builtin_bit_cast(fa_u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+__device__ __forceinline__ float buf_load4f(fa_rsrc r, uint32_t off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+__device__ __forceinline__ void buf_store16(fa_rsrc r, uint32_t off, fa_u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+
 __device__ __forceinline__ void buf_store8(fa_rsrc r, uint32_t off, fa_u32x2 v) {
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(fa_u32x2, v), r, off, 0, 0);
 }

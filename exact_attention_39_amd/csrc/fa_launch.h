@@ -33,7 +33,8 @@ struct BwdArgs {
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t st);
 hipError_t launch_bwd_preprocess(const BwdArgs &a, hipStream_t st);
-hipError_t launch_bwd_main(const BwdArgs &a, hipStream_t st);
+hipError_t launch_bwd_dkdv(const BwdArgs &a, hipStream_t st);
+hipError_t launch_bwd_dq(const BwdArgs &a, hipStream_t st);
 hipError_t launch_exp2_poly(const float *x, float *y, int64_t n, int degree, hipStream_t st);
 
 }  // namespace fa

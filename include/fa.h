@@ -21,8 +21,9 @@
  * idea of the gist.science explainer, section 3 of the German page), and
  * schedules causal tiles longest-first (the LPT causal scheduler of the
  * technical summary, "Belangrijkste Resultaten").  The backward recomputes P
- * tile by tile from the saved LSE and accumulates dQ with global fp32 atomic
- * adds (technical summary, methodology item 3).
+ * tile by tile from the saved LSE (technical summary, methodology item 3);
+ * unlike the pages, which add dQ with global atomics, dQ comes from its own
+ * pass over query blocks, because fp32 atomics are slow on this GPU.
  *
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
@@ -77,12 +78,13 @@ size_t fa_bwd_workspace_bytes(int B, int H, int S, int d);
 
 /*
  * Backward pass for the O and LSE that fa_fwd produced from the same Q, K,
- * V, scale and causal flag.  Writes dQ (fp32 [B][H][S][d]; the library
- * zeroes it first and accumulates into it with atomic adds, so the low bits
- * may differ between runs), dK and dV (bf16 [B][H][S][d]).  workspace must
- * hold at least fa_bwd_workspace_bytes(B, H, S, d) bytes of device memory;
- * its contents on entry are ignored and on return are D.
- * Equivalent to fa_bwd_preprocess followed by fa_bwd_main.
+ * V, scale and causal flag.  Writes dQ (fp32 [B][H][S][d]), dK and dV
+ * (bf16 [B][H][S][d]); every element is written exactly once (no atomics),
+ * so the result is bitwise reproducible.  workspace must hold at least
+ * fa_bwd_workspace_bytes(B, H, S, d) bytes of device memory; its contents on
+ * entry are ignored and on return are D.  Outputs must not overlap inputs.
+ * Equivalent to fa_bwd_preprocess, then fa_bwd_dkdv and fa_bwd_dq (the two
+ * gradient kernels are independent of each other).
  */
 fa_status fa_bwd(const void *Q, const void *K, const void *V, const void *O, const float *LSE,
                  const void *dO, float *dQ, void *dK, void *dV,
@@ -90,22 +92,31 @@ fa_status fa_bwd(const void *Q, const void *K, const void *V, const void *O, con
                  void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * First half of fa_bwd: D_i = sum_k dO_ik O_ik (fp32, into workspace) and
- * dQ := 0.  Same argument rules as fa_bwd.
+ * Step 1 of fa_bwd: D_i = sum_k dO_ik O_ik (fp32, written to workspace).
+ * Same argument rules as fa_bwd.
  */
-fa_status fa_bwd_preprocess(const void *O, const void *dO, float *dQ,
+fa_status fa_bwd_preprocess(const void *O, const void *dO,
                             int B, int H, int S, int d,
                             void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Second half of fa_bwd: recompute P from LSE, accumulate dV, dK and dQ.
- * Expects the workspace D and the zeroed dQ that fa_bwd_preprocess left on
- * the same stream.
+ * Step 2 of fa_bwd: recompute P from LSE tile by tile and write dK and dV
+ * (one workgroup per block of 128 keys).  Reads the D that
+ * fa_bwd_preprocess left in workspace on the same stream.
  */
-fa_status fa_bwd_main(const void *Q, const void *K, const void *V, const float *LSE,
-                      const void *dO, float *dQ, void *dK, void *dV,
+fa_status fa_bwd_dkdv(const void *Q, const void *K, const void *V, const float *LSE,
+                      const void *dO, void *dK, void *dV,
                       int B, int H, int S, int d, float scale, int causal,
                       const void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Step 3 of fa_bwd: recompute P and dP per block of 128 queries and write
+ * dQ = scale * dS K in fp32.  Reads D from workspace like fa_bwd_dkdv.
+ */
+fa_status fa_bwd_dq(const void *Q, const void *K, const void *V, const float *LSE,
+                    const void *dO, float *dQ,
+                    int B, int H, int S, int d, float scale, int causal,
+                    const void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Tuning knobs of the forward softmax, process-wide, read by every later

@@ -87,8 +87,12 @@ def test_backward_checks(lib):
     p[6] = MIS
     assert lib.fa_bwd(*p, 1, 1, 128, 128, ctypes.c_float(0.1), 0, A, 512, NULL) == 1
     assert lib.fa_bwd(*p9, 1, 1, 128, 64 + 1, ctypes.c_float(0.1), 0, A, 512, NULL) == 2
-    assert lib.fa_bwd_main(*([A] * 8), 1, 1, 128, 128, ctypes.c_float(0.1), 3, A, 512, NULL) == 1
-    assert lib.fa_bwd_preprocess(A, A, MIS, 1, 1, 128, 128, A, 512, NULL) == 1
+    assert lib.fa_bwd_dkdv(*([A] * 7), 1, 1, 128, 128, ctypes.c_float(0.1), 3, A, 512, NULL) == 1
+    assert lib.fa_bwd_dkdv(*([A] * 6), MIS, 1, 1, 128, 128, ctypes.c_float(0.1), 0, A, 512, NULL) == 1
+    assert lib.fa_bwd_dq(*([A] * 5), MIS, 1, 1, 128, 128, ctypes.c_float(0.1), 0, A, 512, NULL) == 1
+    assert lib.fa_bwd_dq(*([A] * 6), 1, 1, 128, 128, ctypes.c_float(0.0), 0, A, 512, NULL) == 1
+    assert lib.fa_bwd_preprocess(A, MIS, 1, 1, 128, 128, A, 512, NULL) == 1
+    assert lib.fa_bwd_preprocess(A, A, 1, 1, 128, 128, A, 4, NULL) == 1
 
 
 def test_softmax_options_validation(lib):

@@ -271,3 +271,19 @@ def test_workload_backward_sampled(fa, name, causal):
     cidx = torch.from_numpy(cols).cuda()
     check_grad(bf16_to_np64(dk[b, h, cidx]), gk, f"{name} dK cols")
     check_grad(bf16_to_np64(dv[b, h, cidx]), gv, f"{name} dV cols")
+
+
+def test_backward_is_bitwise_repeatable(fa):
+    """Every gradient element is written once (no atomics): two runs agree bit for bit."""
+    say("[determinism] backward twice")
+    shape = (2, 4, 1000, 128)
+    qb, kb, vb, db = (rand_bits(shape, 500 + i) for i in range(4))
+    scale = 1.0 / np.sqrt(128)
+    for causal in (False, True):
+        q, k, v, o, lse = run_fwd(fa, qb, kb, vb, causal, scale)
+        do = to_dev(db)
+        g1 = fa.backward(q, k, v, o, lse, do, causal=causal, scale=scale)
+        g2 = fa.backward(q, k, v, o, lse, do, causal=causal, scale=scale)
+        torch.cuda.synchronize()
+        for a, b, nm in zip(g1, g2, ("dQ", "dK", "dV")):
+            assert torch.equal(a, b), f"{nm} differs between runs (causal={causal})"

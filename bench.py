@@ -49,16 +49,21 @@ def kernel_source_hash():
 
 def traffic_bytes(kname, causal):
     """HBM bytes per launch of a kernel from the committed counter summary
-    (profiles/traffic_long_s32768.json), or None if absent or taken on other
-    kernel sources."""
+    (profiles/traffic_long_s32768.txt: FETCH_SIZE and WRITE_SIZE of each
+    launch, scaled by what they read for a 1 GiB copy), or None if absent or
+    taken on other kernel sources."""
+    vals = {}
     try:
-        with open(os.path.join(TRAFFIC_DIR, "traffic_long_s32768.json")) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
+        with open(os.path.join(TRAFFIC_DIR, "traffic_long_s32768.txt")) as f:
+            for line in f:
+                parts = line.split()
+                if len(parts) == 2 and not line.startswith("#"):
+                    vals[parts[0]] = parts[1]
+    except OSError:
         return None
-    if t.get("source_sha256") != kernel_source_hash():
+    if vals.get("source_sha256") != kernel_source_hash():
         return None
-    v = t.get("bytes_per_launch", {}).get(f"{kname}{'_causal' if causal else ''}")
+    v = vals.get(f"{kname}{'_causal' if causal else ''}")
     return None if v is None else float(v)
 
 

@@ -136,11 +136,11 @@ def main():
         if kind == "fwd":
             fa.fa_fwd(q, k, v, o, lse, scale, causal, stream)
         elif kind == "bwd_pre":
-            fa.fa_bwd_preprocess(o, do, ws, stream)
+            fa.fa_bwd_preprocess(o, do, lse, ws, stream)
         elif kind == "bwd_dkdv":
-            fa.fa_bwd_dkdv(q, k, v, lse, do, dk, dv, scale, causal, ws, stream)
+            fa.fa_bwd_dkdv(q, k, v, do, dk, dv, scale, causal, ws, stream)
         else:
-            fa.fa_bwd_dq(q, k, v, lse, do, dq, scale, causal, ws, stream)
+            fa.fa_bwd_dq(q, k, v, do, dq, scale, causal, ws, stream)
 
     def step(events=None):
         for i, (kind, causal) in enumerate(parts):
@@ -195,7 +195,7 @@ def main():
              "bwd_dq": "bwd_dq_kernel"}[kind]
     cfac = 0.5 if causal else 1.0
     if kind == "bwd_pre":
-        alg = 2.0 * B * H * S * d * 2 + 4.0 * B * H * S  # bytes: O, dO read; D written
+        alg = 2.0 * B * H * S * d * 2 + 4.0 * B * H * S * 3  # bytes: O, dO, LSE read; D, LSE2 written
         roof = {"bound": "hbm", "achieved": alg / (part_ms[dom] / 1e3) / 1e9, "peak": 8000.0, "unit": "GB/s"}
     else:
         alg = {"fwd": 4.0, "bwd_dkdv": 8.0, "bwd_dq": 2.0}[kind] * B * H * S * S * d * cfac

@@ -45,11 +45,11 @@ def load_library():
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_bwd.restype = i
-    lib.fa_bwd_preprocess.argtypes = [vp, vp, i, i, i, i, vp, sz, vp]
+    lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, vp, sz, vp]
     lib.fa_bwd_preprocess.restype = i
-    lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_bwd_dkdv.restype = i
-    lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_bwd_dq.restype = i
     lib.fa_set_softmax_options.argtypes = [f, i, i]
     lib.fa_set_softmax_options.restype = i
@@ -133,42 +133,44 @@ def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, scale: float, causal: bool, workspac
                                  _ptr(workspace), ws_bytes, _stream(stream)), "fa_bwd")
 
 
-def fa_bwd_preprocess(o, do, workspace, stream=None):
+def fa_bwd_preprocess(o, do, lse, workspace, stream=None):
     import torch
     B, H, S, d = _dims(o)
     _check_tensor(o, "o", torch.bfloat16, (B, H, S, d))
     _check_tensor(do, "do", torch.bfloat16, (B, H, S, d))
+    _check_tensor(lse, "lse", torch.float32, (B, H, S))
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check(load_library().fa_bwd_preprocess(_ptr(o), _ptr(do), B, H, S, d, _ptr(workspace), ws_bytes,
-                                            _stream(stream)), "fa_bwd_preprocess")
+    _check(load_library().fa_bwd_preprocess(_ptr(o), _ptr(do), _ptr(lse), B, H, S, d, _ptr(workspace),
+                                            ws_bytes, _stream(stream)), "fa_bwd_preprocess")
 
 
-def _grad_checks(q, k, v, lse, do):
+def _grad_checks(q, k, v, do):
     import torch
     B, H, S, d = _dims(q)
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (do, "do")):
         _check_tensor(t, nm, torch.bfloat16, (B, H, S, d))
-    _check_tensor(lse, "lse", torch.float32, (B, H, S))
     return B, H, S, d
 
 
-def fa_bwd_dkdv(q, k, v, lse, do, dk, dv, scale: float, causal: bool, workspace, stream=None):
+def fa_bwd_dkdv(q, k, v, do, dk, dv, scale: float, causal: bool, workspace, stream=None):
+    """dK, dV from the workspace that fa_bwd_preprocess filled on the same stream."""
     import torch
-    B, H, S, d = _grad_checks(q, k, v, lse, do)
+    B, H, S, d = _grad_checks(q, k, v, do)
     _check_tensor(dk, "dk", torch.bfloat16, (B, H, S, d))
     _check_tensor(dv, "dv", torch.bfloat16, (B, H, S, d))
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check(load_library().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(do), _ptr(dk), _ptr(dv),
+    _check(load_library().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dk), _ptr(dv),
                                       B, H, S, d, float(scale), int(bool(causal)), _ptr(workspace), ws_bytes,
                                       _stream(stream)), "fa_bwd_dkdv")
 
 
-def fa_bwd_dq(q, k, v, lse, do, dq, scale: float, causal: bool, workspace, stream=None):
+def fa_bwd_dq(q, k, v, do, dq, scale: float, causal: bool, workspace, stream=None):
+    """dQ from the workspace that fa_bwd_preprocess filled on the same stream."""
     import torch
-    B, H, S, d = _grad_checks(q, k, v, lse, do)
+    B, H, S, d = _grad_checks(q, k, v, do)
     _check_tensor(dq, "dq", torch.float32, (B, H, S, d))
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check(load_library().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(do), _ptr(dq), B, H, S, d,
+    _check(load_library().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), B, H, S, d,
                                     float(scale), int(bool(causal)), _ptr(workspace), ws_bytes,
                                     _stream(stream)), "fa_bwd_dq")
 

@@ -93,7 +93,7 @@ fa_status fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LS
 size_t fa_bwd_workspace_bytes(int B, int H, int S, int d) {
     (void)d;
     if (B <= 0 || H <= 0 || S <= 0) return 0;
-    return (size_t)B * (size_t)H * (size_t)S * sizeof(float);
+    return 2 * (size_t)B * (size_t)H * (size_t)S * sizeof(float);
 }
 
 static fa_status check_bwd_common(int B, int H, int S, int d, const void *workspace,
@@ -106,15 +106,16 @@ static fa_status check_bwd_common(int B, int H, int S, int d, const void *worksp
     return FA_OK;
 }
 
-fa_status fa_bwd_preprocess(const void *O, const void *dO, int B, int H, int S, int d,
-                            void *workspace, size_t workspace_bytes, void *stream) {
+fa_status fa_bwd_preprocess(const void *O, const void *dO, const float *LSE, int B, int H, int S,
+                            int d, void *workspace, size_t workspace_bytes, void *stream) {
     bool empty = false;
     fa_status st = check_bwd_common(B, H, S, d, workspace, workspace_bytes, &empty);
     if (st != FA_OK || empty) return st;
-    if (!O || !dO || !aligned16(O) || !aligned16(dO)) return FA_ERR_INVALID;
+    if (!O || !dO || !LSE || !aligned16(O) || !aligned16(dO) || !aligned16(LSE)) return FA_ERR_INVALID;
     fa::BwdArgs a{};
     a.O = O;
     a.dO = dO;
+    a.LSE = LSE;
     a.Dvec = (float *)workspace;
     a.BH = B * H;
     a.S = S;
@@ -123,7 +124,7 @@ fa_status fa_bwd_preprocess(const void *O, const void *dO, int B, int H, int S, 
 }
 
 // Common checks of the two gradient kernels; fills the launch arguments.
-static fa_status bwd_grad_args(const void *Q, const void *K, const void *V, const float *LSE,
+static fa_status bwd_grad_args(const void *Q, const void *K, const void *V,
                                const void *dO, int B, int H, int S, int d, float scale, int causal,
                                const void *workspace, size_t workspace_bytes, fa::BwdArgs *a,
                                bool *empty) {
@@ -131,14 +132,13 @@ static fa_status bwd_grad_args(const void *Q, const void *K, const void *V, cons
     if (st != FA_OK) return st;
     if (!good_scale(scale) || (causal != 0 && causal != 1)) return FA_ERR_INVALID;
     if (*empty) return FA_OK;
-    const void *ptrs[] = {Q, K, V, LSE, dO};
+    const void *ptrs[] = {Q, K, V, dO};
     for (const void *p : ptrs)
         if (!p || !aligned16(p)) return FA_ERR_INVALID;
     *a = fa::BwdArgs{};
     a->Q = Q;
     a->K = K;
     a->V = V;
-    a->LSE = LSE;
     a->dO = dO;
     a->Dvec = (float *)workspace;
     a->BH = B * H;
@@ -149,12 +149,12 @@ static fa_status bwd_grad_args(const void *Q, const void *K, const void *V, cons
     return FA_OK;
 }
 
-fa_status fa_bwd_dkdv(const void *Q, const void *K, const void *V, const float *LSE, const void *dO,
+fa_status fa_bwd_dkdv(const void *Q, const void *K, const void *V, const void *dO,
                       void *dK, void *dV, int B, int H, int S, int d, float scale, int causal,
                       const void *workspace, size_t workspace_bytes, void *stream) {
     fa::BwdArgs a;
     bool empty = false;
-    fa_status st = bwd_grad_args(Q, K, V, LSE, dO, B, H, S, d, scale, causal, workspace,
+    fa_status st = bwd_grad_args(Q, K, V, dO, B, H, S, d, scale, causal, workspace,
                                  workspace_bytes, &a, &empty);
     if (st != FA_OK || empty) return st;
     if (!dK || !dV || !aligned16(dK) || !aligned16(dV)) return FA_ERR_INVALID;
@@ -163,12 +163,12 @@ fa_status fa_bwd_dkdv(const void *Q, const void *K, const void *V, const float *
     return hip_status(fa::launch_bwd_dkdv(a, (hipStream_t)stream));
 }
 
-fa_status fa_bwd_dq(const void *Q, const void *K, const void *V, const float *LSE, const void *dO,
+fa_status fa_bwd_dq(const void *Q, const void *K, const void *V, const void *dO,
                     float *dQ, int B, int H, int S, int d, float scale, int causal,
                     const void *workspace, size_t workspace_bytes, void *stream) {
     fa::BwdArgs a;
     bool empty = false;
-    fa_status st = bwd_grad_args(Q, K, V, LSE, dO, B, H, S, d, scale, causal, workspace,
+    fa_status st = bwd_grad_args(Q, K, V, dO, B, H, S, d, scale, causal, workspace,
                                  workspace_bytes, &a, &empty);
     if (st != FA_OK || empty) return st;
     if (!dQ || !aligned16(dQ)) return FA_ERR_INVALID;
@@ -181,19 +181,17 @@ fa_status fa_bwd(const void *Q, const void *K, const void *V, const void *O, con
                  float scale, int causal, void *workspace, size_t workspace_bytes, void *stream) {
     fa::BwdArgs a;
     bool empty = false;
-    fa_status st = bwd_grad_args(Q, K, V, LSE, dO, B, H, S, d, scale, causal, workspace,
+    fa_status st = bwd_grad_args(Q, K, V, dO, B, H, S, d, scale, causal, workspace,
                                  workspace_bytes, &a, &empty);
     if (st != FA_OK || empty) return st;
-    const void *outs[] = {O, dQ, dK, dV};
+    const void *outs[] = {O, LSE, dQ, dK, dV};
     for (const void *p : outs)
         if (!p || !aligned16(p)) return FA_ERR_INVALID;
-    st = fa_bwd_preprocess(O, dO, B, H, S, d, workspace, workspace_bytes, stream);
+    st = fa_bwd_preprocess(O, dO, LSE, B, H, S, d, workspace, workspace_bytes, stream);
     if (st != FA_OK) return st;
-    st = fa_bwd_dkdv(Q, K, V, LSE, dO, dK, dV, B, H, S, d, scale, causal, workspace, workspace_bytes,
-                     stream);
+    st = fa_bwd_dkdv(Q, K, V, dO, dK, dV, B, H, S, d, scale, causal, workspace, workspace_bytes, stream);
     if (st != FA_OK) return st;
-    return fa_bwd_dq(Q, K, V, LSE, dO, dQ, B, H, S, d, scale, causal, workspace, workspace_bytes,
-                     stream);
+    return fa_bwd_dq(Q, K, V, dO, dQ, B, H, S, d, scale, causal, workspace, workspace_bytes, stream);
 }
 
 fa_status fa_exp2_poly(const float *x, float *y, int64_t n, int degree, void *stream) {

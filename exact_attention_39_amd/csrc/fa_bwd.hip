@@ -20,13 +20,15 @@
 // instead of 5) but writes dQ once with plain stores.  The backward is then
 // free of atomics and bitwise deterministic.
 //
-// dK/dV kernel: one workgroup = 4 waves = 128 key rows (32 per wave); K and
-// V rows stay resident as MFMA B operands in registers, dK and dV
-// accumulate in registers; query blocks of 64 rows (Q, dO, LSE, D) stream
-// through a double-buffered LDS stage filled by direct memory-to-LDS copies.
-// Per wave and block: S = Q K^T and dP = dO V^T (keys on the lanes), P and
-// dS in registers, dV += P^T dO and dK += dS^T Q with P and dS fed straight
-// from the accumulators and dO, Q through transposing LDS reads.
+// dK/dV kernel: one workgroup = 8 waves = 128 key rows; each pair of waves
+// (one per SIMD half) owns 32 keys and splits every 64-row query block in
+// two, so each SIMD holds two waves that overlap MFMA with softmax work.  K
+// and V of the block stay in LDS, dK and dV accumulate in registers; query
+// blocks (Q, dO, LSE, D) stream through a double-buffered LDS stage filled by
+// direct memory-to-LDS copies.  Per wave and block: S = Q K^T and
+// dP = dO V^T (keys on the lanes), P and dS in registers, dV += P^T dO and
+// dK += dS^T Q with P and dS fed straight from the accumulators and dO, Q
+// through transposing LDS reads.
 //
 // dQ kernel: one workgroup = 4 waves = 128 query rows (32 per wave), two
 // workgroups per CU; Q and dO rows resident as B operands, keys/values
@@ -38,6 +40,8 @@
 // Causal: key blocks only meet query blocks at or below the diagonal; both
 // kernels order workgroup ids so the longest blocks start first (LPT,
 // technical summary, results).
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -51,10 +55,14 @@ constexpr int kQPerIter = 64;     // dK/dV kernel: query rows per iteration
 constexpr int kQPerBlock = 128;   // dQ kernel: query rows per workgroup
 constexpr int kKvPerTile = 64;    // dQ kernel: key rows per tile
 
+// D_i = sum_k dO_ik O_ik and LSE_i * log2(e) (the base-2 exponent offset the
+// two gradient kernels use), both into the workspace.
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const uint16_t *__restrict__ O,
                                                            const uint16_t *__restrict__ dO,
-                                                           float *__restrict__ Dvec, int64_t rows) {
+                                                           const float *__restrict__ LSE,
+                                                           float *__restrict__ Dvec,
+                                                           float *__restrict__ L2vec, int64_t rows) {
     constexpr int LPR = D / 8;  // lanes per row, 8 elements each
     constexpr int RPB = kThreads / LPR;
     const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
@@ -71,52 +79,59 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const uint16_t *__res
     }
 #pragma unroll
     for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (row < rows && part == 0) Dvec[row] = acc;
+    if (row < rows && part == 0) {
+        Dvec[row] = acc;
+        L2vec[row] = LSE[row] * FA_LOG2E;
+    }
 }
 
 // ---------------------------------------------------------------- dK, dV
+// 8 waves: wave w owns keys 32 (w % 4) .. +31 of the block and query half
+// w / 4 of every 64-row query block, so two waves on each SIMD interleave.
+// K and V of the block sit in LDS; the two waves that share keys add their
+// dK, dV partials through LDS once, at the end.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
-    const float *__restrict__ LSE, const float *__restrict__ Dvec, const uint16_t *__restrict__ dO,
+    const float *__restrict__ L2vec, const float *__restrict__ Dvec, const uint16_t *__restrict__ dO,
     uint16_t *__restrict__ dK, uint16_t *__restrict__ dV, int BH, int S, float scale, float c) {
+    constexpr int NW = 8;
     constexpr int ROWB = D * 2;
     constexpr int NCH = ROWB / 16;
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
     constexpr int QTILE = kQPerIter * ROWB;
+    constexpr int KTILE = kKvPerBlock * ROWB;
+    constexpr int SMEM = 2 * KTILE + 4 * QTILE + 4 * kQPerIter * 4;
+    static_assert(SMEM >= 4 * 2 * DB * 16 * 64 * 4, "epilogue exchange must fit in LDS");
 
-    __shared__ __attribute__((aligned(1024))) char smem_raw[4 * QTILE + 4 * kQPerIter * 4];
+    __shared__ __attribute__((aligned(1024))) char smem_raw[SMEM];
     fa_lds_char *smem = (fa_lds_char *)smem_raw;
-    fa_lds_char *sQ0 = smem;                     // [2] Q tiles
+    fa_lds_char *sK = smem;                      // K rows of the block
+    fa_lds_char *sV = sK + KTILE;                // V rows of the block
+    fa_lds_char *sQ0 = sV + KTILE;               // [2] Q tiles
     fa_lds_char *sO0 = sQ0 + 2 * QTILE;          // [2] dO tiles
     fa_lds_char *sLD = sO0 + 2 * QTILE;          // [2][LSE 64 | D 64] floats
 
     const int lane = threadIdx.x & 63, w = wave_id();
     const int h = lane >> 5, n = lane & 31;
+    const int kw = w & 3;   // key slice of this wave
+    const int qh = w >> 2;  // query half of this wave
 
     const int bh = blockIdx.x % BH;
     const int kblk = blockIdx.x / BH;
     const int k0 = kblk * kKvPerBlock;
     const size_t head = (size_t)bh * (size_t)S * D;
-    const int kv = k0 + 32 * w + n;  // this lane's key for S and dP
+    const int kv = k0 + 32 * kw + n;  // this lane's key for S and dP
 
     const uint32_t head_bytes = (uint32_t)S * ROWB;
     const fa_rsrc rQ = make_rsrc(Q + head, head_bytes);
-    const fa_rsrc rK = make_rsrc(K + head, head_bytes);
-    const fa_rsrc rV = make_rsrc(V + head, head_bytes);
     const fa_rsrc rdO = make_rsrc(dO + head, head_bytes);
-    const fa_rsrc rL = make_rsrc(LSE + (size_t)bh * S, (uint32_t)S * 4);
+    const fa_rsrc rL = make_rsrc(L2vec + (size_t)bh * S, (uint32_t)S * 4);
     const fa_rsrc rD = make_rsrc(Dvec + (size_t)bh * S, (uint32_t)S * 4);
 
-    // Resident B operands: K[kv][16ks + 8h ..] and V[kv][..] (zero past S).
-    fa_u32x4 kf[KS], vf[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        const uint32_t off = (uint32_t)kv * ROWB + (16 * ks + 8 * h) * 2;
-        kf[ks] = buf_load16(rK, off);
-        vf[ks] = buf_load16(rV, off);
-    }
+    tile_to_lds<NCH, kKvPerBlock, NW>(make_rsrc(K + head, head_bytes), k0, sK, w, lane);
+    tile_to_lds<NCH, kKvPerBlock, NW>(make_rsrc(V + head, head_bytes), k0, sV, w, lane);
 
     fa_f32x16 dkacc[DB], dvacc[DB];
 #pragma unroll
@@ -132,8 +147,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     // and D (wave 1).  Rows past S arrive as zeros; such rows then carry
     // dO = 0 and D = 0, so they add nothing to dV or dK.
     auto issue = [&](int i, int buf) {
-        tile_to_lds<NCH, kQPerIter>(rQ, i * kQPerIter, sQ0 + buf * QTILE, w, lane);
-        tile_to_lds<NCH, kQPerIter>(rdO, i * kQPerIter, sO0 + buf * QTILE, w, lane);
+        tile_to_lds<NCH, kQPerIter, NW>(rQ, i * kQPerIter, sQ0 + buf * QTILE, w, lane);
+        tile_to_lds<NCH, kQPerIter, NW>(rdO, i * kQPerIter, sO0 + buf * QTILE, w, lane);
         if (w < 2) {
             fa_lds_char *dst = sLD + (buf * 2 + w) * kQPerIter * 4;
             buf_load_lds<4>(w == 0 ? rL : rD, dst, (uint32_t)(i * kQPerIter + lane) * 4);
@@ -144,86 +159,128 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     wait_vmem();
     __syncthreads();
 
-    for (int i = ib; i < nqb; ++i) {
-        const int buf = (i - ib) & 1;
-        if (i + 1 < nqb) issue(i + 1, buf ^ 1);
-        const int q0 = i * kQPerIter;
+    // Lane-dependent LDS offsets, computed once (see the forward kernel):
+    // row reads of query row 32 qh + n and key row 32 kw + n at chunk
+    // 2 ks + h, and transposing reads of query rows 32 qh + 16 t + 4 h +
+    // 8 s + L/4 (t is an immediate).
+    int qoff[KS], koff[KS], troff[DB][2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        qoff[ks] = tile_off<NCH>(32 * qh + n, (2 * ks + h) * 16);
+        koff[ks] = tile_off<NCH>(32 * kw + n, (2 * ks + h) * 16);
+    }
+    {
+        const int L = lane & 15;
+        const int col = ((lane >> 4) & 1) * 16 + (L & 3) * 4;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+                troff[db][s2] = tile_off<NCH>(32 * qh + 4 * h + 8 * s2 + (L >> 2), (32 * db + col) * 2);
+    }
+
+    // One query block.  MASK: causal blocks that cross this key block's
+    // diagonal.  Keys at or past S need no mask here: they only feed dK, dV
+    // rows that are never stored.
+    auto compute_block = [&](int buf, int q0, auto MASKC) {
+        constexpr bool MASK = decltype(MASKC)::value;
         const fa_lds_char *sQ = sQ0 + buf * QTILE;
         const fa_lds_char *sO = sO0 + buf * QTILE;
         const fa_lds_char *sL = sLD + buf * 2 * kQPerIter * 4;
         const fa_lds_char *sD = sL + kQPerIter * 4;
 
-        // S = Q K^T and dP = dO V^T: 64 queries x this wave's 32 keys.
-        fa_f32x16 sacc[2] = {zero16(), zero16()};
-        fa_f32x16 pacc[2] = {zero16(), zero16()};
+        // S = Q K^T and dP = dO V^T: this wave's 32 queries x its 32 keys.
+        fa_f32x16 sacc = zero16(), pacc = zero16();
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                const int off = tile_off<NCH>(32 * qb + n, (2 * ks + h) * 16);
-                sacc[qb] = mfma32(lds_read16(sQ, off), kf[ks], sacc[qb]);
-                pacc[qb] = mfma32(lds_read16(sO, off), vf[ks], pacc[qb]);
-            }
+            sacc = mfma32(lds_read16(sQ, qoff[ks]), lds_read16(sK, koff[ks]), sacc);
+            pacc = mfma32(lds_read16(sO, qoff[ks]), lds_read16(sV, koff[ks]), pacc);
         }
 
-        // P = 2^(s c - LSE log2 e) (masked -> 0), dS = scale P (dP - D).
-        const bool need_mask = (CAUSAL && q0 < k0 + kKvPerBlock - 1) || (k0 + kKvPerBlock > S);
-        fa_u32x4 pf[4], dsf[4];
+        // P = 2^(s c - LSE log2 e) (masked -> 0), dS = P (dP - D); the
+        // factor scale of dS is applied to dK once, at the end.
+        fa_u32x4 pf[2], dsf[2];
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int g = 0; g < 4; ++g) {
+            const int qi = 32 * qh + 8 * g + 4 * h;
+            const fa_f32x4 l4 = *(const __attribute__((address_space(3))) fa_f32x4 *)(sL + qi * 4);
+            const fa_f32x4 d4 = *(const __attribute__((address_space(3))) fa_f32x4 *)(sD + qi * 4);
+            float p[4], ds[4];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int qi = 32 * qb + 8 * g + 4 * h;
-                const fa_f32x4 l4 = *(const __attribute__((address_space(3))) fa_f32x4 *)(sL + qi * 4);
-                const fa_f32x4 d4 = *(const __attribute__((address_space(3))) fa_f32x4 *)(sD + qi * 4);
-                float p[4], ds[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * g + e;
-                    float pv = __builtin_amdgcn_exp2f(fmaf(sacc[qb][r], c, -l4[e] * FA_LOG2E));
-                    if (need_mask) {
-                        const int q = q0 + qi + e;
-                        const bool dead = (CAUSAL && kv > q) || kv >= S;
-                        pv = dead ? 0.0f : pv;
-                    }
-                    p[e] = pv;
-                    ds[e] = pv * (pacc[qb][r] - d4[e]) * scale;
-                }
-                const int t = 2 * qb + (g >> 1);
-                const int wd = (g & 1) * 2;
-                pf[t][wd] = pack_bf16(p[0], p[1]);
-                pf[t][wd + 1] = pack_bf16(p[2], p[3]);
-                dsf[t][wd] = pack_bf16(ds[0], ds[1]);
-                dsf[t][wd + 1] = pack_bf16(ds[2], ds[3]);
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g + e;
+                float pv = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, -l4[e]));
+                if constexpr (MASK) pv = kv > q0 + qi + e ? 0.0f : pv;
+                p[e] = pv;
+                ds[e] = pv * (pacc[r] - d4[e]);
             }
+            const int t = g >> 1;
+            const int wd = (g & 1) * 2;
+            pf[t][wd] = pack_bf16(p[0], p[1]);
+            pf[t][wd + 1] = pack_bf16(p[2], p[3]);
+            dsf[t][wd] = pack_bf16(ds[0], ds[1]);
+            dsf[t][wd + 1] = pack_bf16(ds[2], ds[3]);
         }
 
-        // dV += P^T dO and dK += dS^T Q; query order of k-step t follows the
-        // accumulator rows: 16t + 8(j/4) + 4h + j%4.
+        // dV += P^T dO and dK += dS^T Q over this wave's 32 queries; query
+        // order of k-step t follows the accumulator rows 16t + 8(j/4) + 4h + j%4.
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int rbase = 16 * t + 4 * h;
+        for (int t = 0; t < 2; ++t) {
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                dvacc[db] = mfma32(pf[t], operand_tr<NCH>(sO, rbase, rbase + 8, 32 * db, lane), dvacc[db]);
-                dkacc[db] = mfma32(dsf[t], operand_tr<NCH>(sQ, rbase, rbase + 8, 32 * db, lane), dkacc[db]);
+                const fa_u32x2 o0 = lds_read_tr(sO + 16 * t * ROWB, troff[db][0]);
+                const fa_u32x2 o1 = lds_read_tr(sO + 16 * t * ROWB, troff[db][1]);
+                const fa_u32x2 q0r = lds_read_tr(sQ + 16 * t * ROWB, troff[db][0]);
+                const fa_u32x2 q1r = lds_read_tr(sQ + 16 * t * ROWB, troff[db][1]);
+                const fa_u32x4 bo = {o0[0], o0[1], o1[0], o1[1]};
+                const fa_u32x4 bq = {q0r[0], q0r[1], q1r[0], q1r[1]};
+                dvacc[db] = mfma32(pf[t], bo, dvacc[db]);
+                dkacc[db] = mfma32(dsf[t], bq, dkacc[db]);
             }
         }
+    };
+
+    auto step = [&](int i, auto MASKC) {
+        const int buf = (i - ib) & 1;
+        if (i + 1 < nqb) issue(i + 1, buf ^ 1);
+        compute_block(buf, i * kQPerIter, MASKC);
         wait_vmem();      // next query block has landed
         __syncthreads();  // ... for every wave, and this block's stage is free
-    }
+    };
 
-    // Epilogue: dK, dV rows of this workgroup (lane = d column, registers = keys).
-    const fa_rsrc rdK = make_rsrc(dK + head, head_bytes);
-    const fa_rsrc rdV = make_rsrc(dV + head, head_bytes);
+    // causal: the first two query blocks cross the diagonal of this key block
+    const int i_plain = CAUSAL ? min(nqb, (k0 + kKvPerBlock - 1) / kQPerIter + 1) : ib;
+    for (int i = ib; i < i_plain; ++i) step(i, std::true_type{});
+    for (int i = i_plain; i < nqb; ++i) step(i, std::false_type{});
+
+    // Epilogue: the upper query half hands its partials to the lower half
+    // through LDS (all stages are free now), which adds and stores.
+    // Layout per key slice kw: [dV | dK][db][r][lane] fp32.
+    fa_lds_char *xch = smem + kw * (2 * DB * 16 * 64 * 4);
+    if (qh == 1) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int kr = k0 + 32 * w + 8 * (r >> 2) + 4 * h + (r & 3);
-            const uint32_t off = ((uint32_t)kr * D + 32 * db + n) * 2;
-            buf_store2(rdK, off, (uint16_t)(pack_bf16(dkacc[db][r], 0.0f) & 0xFFFFu));
-            buf_store2(rdV, off, (uint16_t)(pack_bf16(dvacc[db][r], 0.0f) & 0xFFFFu));
+            for (int r = 0; r < 16; ++r) {
+                *(__attribute__((address_space(3))) float *)(xch + (((0 * DB + db) * 16 + r) * 64 + lane) * 4) = dvacc[db][r];
+                *(__attribute__((address_space(3))) float *)(xch + (((1 * DB + db) * 16 + r) * 64 + lane) * 4) = dkacc[db][r];
+            }
+    }
+    __syncthreads();
+    if (qh == 0) {
+        const fa_rsrc rdK = make_rsrc(dK + head, head_bytes);
+        const fa_rsrc rdV = make_rsrc(dV + head, head_bytes);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float v = dvacc[db][r] + *(const __attribute__((address_space(3))) float *)(xch + (((0 * DB + db) * 16 + r) * 64 + lane) * 4);
+                const float k = (dkacc[db][r] + *(const __attribute__((address_space(3))) float *)(xch + (((1 * DB + db) * 16 + r) * 64 + lane) * 4)) * scale;
+                const int kr = k0 + 32 * kw + 8 * (r >> 2) + 4 * h + (r & 3);
+                const uint32_t off = ((uint32_t)kr * D + 32 * db + n) * 2;
+                buf_store2(rdK, off, (uint16_t)(pack_bf16(k, 0.0f) & 0xFFFFu));
+                buf_store2(rdV, off, (uint16_t)(pack_bf16(v, 0.0f) & 0xFFFFu));
+            }
         }
     }
 }
@@ -232,7 +289,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
-    const float *__restrict__ LSE, const float *__restrict__ Dvec, const uint16_t *__restrict__ dO,
+    const float *__restrict__ L2vec, const float *__restrict__ Dvec, const uint16_t *__restrict__ dO,
     float *__restrict__ dQ, int BH, int S, float scale, float c, int nqb) {
     constexpr int ROWB = D * 2;
     constexpr int NCH = ROWB / 16;
@@ -271,8 +328,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         qf[ks] = buf_load16(rQ, off);
         of[ks] = buf_load16(rdO, off);
     }
-    const float lse2 =
-        buf_load4f(make_rsrc(LSE + (size_t)bh * S, (uint32_t)S * 4), (uint32_t)qrow * 4) * FA_LOG2E;
+    const float lse2 = buf_load4f(make_rsrc(L2vec + (size_t)bh * S, (uint32_t)S * 4), (uint32_t)qrow * 4);
     const float dd = buf_load4f(make_rsrc(Dvec + (size_t)bh * S, (uint32_t)S * 4), (uint32_t)qrow * 4);
 
     fa_f32x16 dqacc[DB];
@@ -285,63 +341,89 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         tile_to_lds<NCH, kKvPerTile>(rV, j * kKvPerTile, sK + TILE, w, lane);
     };
 
+    // Lane-dependent LDS offsets, computed once (as in the forward kernel).
+    int koff[KS], troff[DB][2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) koff[ks] = tile_off<NCH>(n, (2 * ks + h) * 16);
+    {
+        const int L = lane & 15;
+        const int col = ((lane >> 4) & 1) * 16 + (L & 3) * 4;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+                troff[db][s2] = tile_off<NCH>(4 * h + 8 * s2 + (L >> 2), (32 * db + col) * 2);
+    }
+
+    // One 64-key tile.  MASK: the tile crosses this wave's diagonal or the
+    // end of the sequence.  The factor scale of dS is applied to dQ at the end.
+    auto compute_tile = [&](int buf, int kv0, auto MASKC) {
+        constexpr bool MASK = decltype(MASKC)::value;
+        const fa_lds_char *sK = smem + buf * 2 * TILE;
+        const fa_lds_char *sV = sK + TILE;
+        // S^T = K Q^T and dP^T = V dO^T: 64 keys x 32 queries each.
+        fa_f32x16 sacc[2] = {zero16(), zero16()};
+        fa_f32x16 pacc[2] = {zero16(), zero16()};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                sacc[mb] = mfma32(lds_read16(sK + 32 * mb * ROWB, koff[ks]), qf[ks], sacc[mb]);
+                pacc[mb] = mfma32(lds_read16(sV + 32 * mb * ROWB, koff[ks]), of[ks], pacc[mb]);
+            }
+        }
+        fa_u32x4 dsf[4];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                float ds[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    float pv = __builtin_amdgcn_exp2f(fmaf(sacc[mb][r + e], c, -lse2));
+                    if constexpr (MASK) {
+                        const int key = kv0 + 32 * mb + 8 * ((r + e) >> 2) + 4 * h + ((r + e) & 3);
+                        const bool dead = (CAUSAL && key > qrow) || key >= S;
+                        pv = dead ? 0.0f : pv;
+                    }
+                    ds[e] = pv * (pacc[mb][r + e] - dd);
+                }
+                dsf[2 * mb + (r >> 3)][(r & 7) >> 1] = pack_bf16(ds[0], ds[1]);
+            }
+        }
+        // dQ^T += K^T dS^T, keys of k-step t in accumulator order.
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const fa_u32x2 lo = lds_read_tr(sK + 16 * t * ROWB, troff[db][0]);
+                const fa_u32x2 hi = lds_read_tr(sK + 16 * t * ROWB, troff[db][1]);
+                const fa_u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+                dqacc[db] = mfma32(a, dsf[t], dqacc[db]);
+            }
+        }
+    };
+
+    auto step = [&](int j, auto MASKC) {
+        const int buf = j & 1;
+        if (j + 1 < nkv) issue_tile(j + 1, buf ^ 1);
+        const int kv0 = j * kKvPerTile;
+        if constexpr (decltype(MASKC)::value) {
+            if (!(CAUSAL && kv0 > wq_lo + 31)) compute_tile(buf, kv0, MASKC);
+        } else {
+            compute_tile(buf, kv0, MASKC);
+        }
+        wait_vmem();
+        __syncthreads();
+    };
+
     if (nkv > 0) issue_tile(0, 0);
     wait_vmem();
     __syncthreads();
 
-    for (int j = 0; j < nkv; ++j) {
-        const int buf = j & 1;
-        if (j + 1 < nkv) issue_tile(j + 1, buf ^ 1);
-        const fa_lds_char *sK = smem + buf * 2 * TILE;
-        const fa_lds_char *sV = sK + TILE;
-        const int kv0 = j * kKvPerTile;
-        const bool skip = CAUSAL && (kv0 > wq_lo + 31);
-
-        if (!skip) {
-            // S^T = K Q^T and dP^T = V dO^T: 64 keys x 32 queries each.
-            fa_f32x16 sacc[2] = {zero16(), zero16()};
-            fa_f32x16 pacc[2] = {zero16(), zero16()};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-                for (int mb = 0; mb < 2; ++mb) {
-                    const int off = tile_off<NCH>(32 * mb + n, (2 * ks + h) * 16);
-                    sacc[mb] = mfma32(lds_read16(sK, off), qf[ks], sacc[mb]);
-                    pacc[mb] = mfma32(lds_read16(sV, off), of[ks], pacc[mb]);
-                }
-            }
-            const bool need_mask = (CAUSAL && (kv0 + kKvPerTile - 1 > wq_lo)) || (kv0 + kKvPerTile > S);
-            fa_u32x4 dsf[4];
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    float ds[2];
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        float pv = __builtin_amdgcn_exp2f(fmaf(sacc[mb][r + e], c, -lse2));
-                        if (need_mask) {
-                            const int key = kv0 + 32 * mb + 8 * ((r + e) >> 2) + 4 * h + ((r + e) & 3);
-                            const bool dead = (CAUSAL && key > qrow) || key >= S;
-                            pv = dead ? 0.0f : pv;
-                        }
-                        ds[e] = pv * (pacc[mb][r + e] - dd) * scale;
-                    }
-                    dsf[2 * mb + (r >> 3)][(r & 7) >> 1] = pack_bf16(ds[0], ds[1]);
-                }
-            }
-            // dQ^T += K^T dS^T, keys of k-step t in accumulator order.
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int rbase = 16 * t + 4 * h;
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-                    dqacc[db] = mfma32(operand_tr<NCH>(sK, rbase, rbase + 8, 32 * db, lane), dsf[t], dqacc[db]);
-            }
-        }
-        wait_vmem();
-        __syncthreads();
-    }
+    const int n_plain = min(nkv, (CAUSAL ? min(q0, S) : S) / kKvPerTile);
+    for (int j = 0; j < n_plain; ++j) step(j, std::false_type{});
+    for (int j = n_plain; j < nkv; ++j) step(j, std::true_type{});
 
     // Epilogue: lane = query row, registers = 4 consecutive d per group.
     const fa_rsrc rdQ = make_rsrc(dQ + head, (uint32_t)S * D * 4);
@@ -349,8 +431,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            fa_u32x4 v = {__float_as_uint(dqacc[db][4 * g]), __float_as_uint(dqacc[db][4 * g + 1]),
-                          __float_as_uint(dqacc[db][4 * g + 2]), __float_as_uint(dqacc[db][4 * g + 3])};
+            fa_u32x4 v = {__float_as_uint(dqacc[db][4 * g] * scale), __float_as_uint(dqacc[db][4 * g + 1] * scale),
+                          __float_as_uint(dqacc[db][4 * g + 2] * scale), __float_as_uint(dqacc[db][4 * g + 3] * scale)};
             buf_store16(rdQ, ((uint32_t)qrow * D + 32 * db + 8 * g + 4 * h) * 4, v);
         }
 }
@@ -361,16 +443,17 @@ hipError_t launch_pre_d(const BwdArgs &a, hipStream_t st) {
     const int64_t rows = (int64_t)a.BH * a.S;
     const dim3 grid((unsigned)((rows + RPB - 1) / RPB)), block(kThreads);
     hipLaunchKernelGGL((bwd_pre_kernel<D>), grid, block, 0, st, (const uint16_t *)a.O,
-                       (const uint16_t *)a.dO, a.Dvec, rows);
+                       (const uint16_t *)a.dO, a.LSE, a.Dvec, a.Dvec + rows, rows);
     return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_dkdv_t(const BwdArgs &a, hipStream_t st) {
     const int nkb = (a.S + kKvPerBlock - 1) / kKvPerBlock;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(a.BH * nkb)), dim3(kThreads), 0, st,
-                       (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V, a.LSE,
-                       (const float *)a.Dvec, (const uint16_t *)a.dO, (uint16_t *)a.dK, (uint16_t *)a.dV,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(a.BH * nkb)), dim3(2 * kThreads), 0, st,
+                       (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
+                       (const float *)a.Dvec + (size_t)a.BH * a.S, (const float *)a.Dvec,
+                       (const uint16_t *)a.dO, (uint16_t *)a.dK, (uint16_t *)a.dV,
                        a.BH, a.S, a.scale, a.scale * FA_LOG2E);
     return hipGetLastError();
 }
@@ -379,8 +462,9 @@ template <int D, bool CAUSAL>
 hipError_t launch_dq_t(const BwdArgs &a, hipStream_t st) {
     const int nqb = (a.S + kQPerBlock - 1) / kQPerBlock;
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(a.BH * nqb)), dim3(kThreads), 0, st,
-                       (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V, a.LSE,
-                       (const float *)a.Dvec, (const uint16_t *)a.dO, a.dQ, a.BH, a.S, a.scale,
+                       (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
+                       (const float *)a.Dvec + (size_t)a.BH * a.S, (const float *)a.Dvec,
+                       (const uint16_t *)a.dO, a.dQ, a.BH, a.S, a.scale,
                        a.scale * FA_LOG2E, nqb);
     return hipGetLastError();
 }

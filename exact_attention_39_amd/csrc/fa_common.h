@@ -134,19 +134,20 @@ __device__ __forceinline__ int swz(int row) {
 
 // Copy ROWS rows of a row-major global matrix (row pitch NCH*16 bytes,
 // starting at byte offset row0 * pitch of the resource) into a swizzled LDS
-// tile with 4 waves (w = wave index, wave-uniform), straight from memory to LDS.  Each wave instruction
-// fills 1 KB of LDS contiguously, so the swizzle is applied on the global
-// side: the lane that owns physical chunk pc of a row fetches logical chunk
-// pc ^ swz(row).  Rows past the resource end arrive as zeros.
-template <int NCH, int ROWS>
+// tile with NW waves (w = wave index, wave-uniform), straight from memory to
+// LDS.  Each wave instruction fills 1 KB of LDS contiguously, so the swizzle
+// is applied on the global side: the lane that owns physical chunk pc of a
+// row fetches logical chunk pc ^ swz(row).  Rows past the resource end
+// arrive as zeros.
+template <int NCH, int ROWS, int NW = 4>
 __device__ __forceinline__ void tile_to_lds(fa_rsrc r, int row0, fa_lds_char *tile, int w, int lane) {
     constexpr int ROWB = NCH * 16;
     constexpr int ROWS_PER_INST = 1024 / ROWB;
     constexpr int INSTS = ROWS * ROWB / 1024;   // wave instructions for the tile
-    static_assert(INSTS % 4 == 0, "tile must split evenly over 4 waves");
+    static_assert(INSTS % NW == 0, "tile must split evenly over the waves");
 #pragma unroll
-    for (int k = 0; k < INSTS / 4; ++k) {
-        const int inst = w + 4 * k;
+    for (int k = 0; k < INSTS / NW; ++k) {
+        const int inst = w + NW * k;
         const int row = inst * ROWS_PER_INST + lane / NCH;
         const int pc = lane % NCH;
         const int c = pc ^ swz<NCH>(row);

@@ -34,6 +34,8 @@
 //     (technical summary, methodology item 2);
 //   * causal tiles are processed longest first: workgroup ids map to the
 //     last query blocks first (LPT, technical summary, results).
+#include <type_traits>
+
 #include "fa_common.h"
 #include "exp2_poly.h"
 #include "fa_launch.h"
@@ -105,86 +107,126 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(
         tile_to_lds<NCH, kBc>(rV, j * kBc, sK + TILE, w, lane);
     };
 
+    // Lane-dependent LDS offsets, computed once.  Row reads of key row
+    // 32 mb + n at chunk 2 ks + h: the swizzle only sees the low 4 bits of
+    // the row, so mb is an immediate (32 rows) and one offset per ks remains.
+    // Transposing reads of V rows 16 t + 4 h + 8 s + L/4: the swizzle is the
+    // same for every t, so t is an immediate and one offset per (db, s)
+    // remains.
+    int koff[KS], voff[DB][2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) koff[ks] = tile_off<NCH>(n, (2 * ks + h) * 16);
+    {
+        const int L = lane & 15;
+        const int col = ((lane >> 4) & 1) * 16 + (L & 3) * 4;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) voff[db][s2] = tile_off<NCH>(4 * h + 8 * s2 + (L >> 2), (32 * db + col) * 2);
+    }
+
+    // One key/value tile from LDS buffer BUF (a compile-time constant, so
+    // every LDS address is a loop-invariant register plus an immediate).
+    // MASK: the tile crosses this wave's diagonal or the end of the sequence.
+    auto compute_tile = [&](int buf, auto MASKC, int kv0) {
+        constexpr bool MASK = decltype(MASKC)::value;
+        const fa_lds_char *sK = smem + buf * 2 * TILE;
+        const fa_lds_char *sV = sK + TILE;
+        // S^T = K Q^T for 64 keys x 32 queries: two 32x32 blocks.
+        fa_f32x16 sacc[2] = {zero16(), zero16()};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                const fa_u32x4 a = lds_read16(sK + 32 * mb * ROWB, koff[ks]);
+                sacc[mb] = mfma32(a, qf[ks], sacc[mb]);
+            }
+        }
+        if constexpr (MASK) {
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int kv = kv0 + 32 * mb + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const bool dead = (CAUSAL && kv > qrow) || kv >= S;
+                    sacc[mb][r] = dead ? -INFINITY : sacc[mb][r];
+                }
+        }
+        // row max over this lane's 32 keys, then across the two half-waves
+        float mx = sacc[0][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][r]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][r]);
+        mx = max_halves(mx);
+        const float m_new = mx * c;
+        const bool need = m_new > m_ref + tau;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+            const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
+            m_ref = need ? m_new : m_ref;
+            l_sum *= alpha;
+#pragma unroll
+            for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
+        }
+        const float nm = -m_ref;
+        // P = 2^(s c - m_ref), packed to bf16 in MFMA k order.  The row sum
+        // adds the fp32 values (two partial sums): summing the bf16-rounded
+        // ones would put up to 2^-9 relative error into the LSE of rows with
+        // few keys.
+        fa_u32x4 pf[4];
+        float la = 0.0f, lb = 0.0f;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float p0 = exp2_sel<POLY, DEG>(fmaf(sacc[mb][r], c, nm), r);
+                const float p1 = exp2_sel<POLY, DEG>(fmaf(sacc[mb][r + 1], c, nm), r + 1);
+                la += p0;
+                lb += p1;
+                pf[2 * mb + (r >> 3)][(r & 7) >> 1] = pack_bf16(p0, p1);
+            }
+        }
+        l_sum += la + lb;
+        // O^T += V^T P^T, k-step t covers keys 16t .. 16t+15 of the tile in
+        // accumulator order; V^T operand by transposing reads of V rows.
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const fa_u32x2 lo = lds_read_tr(sV + 16 * t * ROWB, voff[db][0]);
+                const fa_u32x2 hi = lds_read_tr(sV + 16 * t * ROWB, voff[db][1]);
+                const fa_u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+                oacc[db] = mfma32(a, pf[t], oacc[db]);
+            }
+        }
+    };
+
+    // One loop step: prefetch tile j+1 into the other buffer, compute tile j,
+    // then wait for the prefetch and synchronise.  Interior tiles (no key
+    // past the diagonal of any row of the workgroup, none past S) run
+    // without masking in a first loop; the at most two boundary tiles run
+    // masked in a second loop, where a wave whose rows all lie above the
+    // tile skips the compute.
+    auto step = [&](int j, auto MASKC) {
+        const int buf = j & 1;
+        if (j + 1 < nkv) issue_tile(j + 1, buf ^ 1);
+        const int kv0 = j * kBc;
+        if constexpr (decltype(MASKC)::value) {
+            if (!(CAUSAL && kv0 > wq_lo + 31)) compute_tile(buf, MASKC, kv0);
+        } else {
+            compute_tile(buf, MASKC, kv0);
+        }
+        wait_vmem();      // tile j+1 has landed in the other buffer
+        __syncthreads();  // ... for every wave, and nobody still reads this one
+    };
+
     if (nkv > 0) issue_tile(0, 0);
     wait_vmem();
     __syncthreads();
 
-    for (int j = 0; j < nkv; ++j) {
-        const int buf = j & 1;
-        if (j + 1 < nkv) issue_tile(j + 1, buf ^ 1);
-        const fa_lds_char *sK = smem + buf * 2 * TILE;
-        const fa_lds_char *sV = sK + TILE;
-        const int kv0 = j * kBc;
-        const bool skip = CAUSAL && (kv0 > wq_lo + 31);  // whole tile above this wave's diagonal
-
-        if (!skip) {
-            // S^T = K Q^T for 64 keys x 32 queries: two 32x32 blocks.
-            fa_f32x16 sacc[2] = {zero16(), zero16()};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-                for (int mb = 0; mb < 2; ++mb) {
-                    const fa_u32x4 a = lds_read16(sK, tile_off<NCH>(32 * mb + n, (2 * ks + h) * 16));
-                    sacc[mb] = mfma32(a, qf[ks], sacc[mb]);
-                }
-            }
-            const bool need_mask = (CAUSAL && (kv0 + kBc - 1 > wq_lo)) || (kv0 + kBc > S);
-            if (need_mask) {
-#pragma unroll
-                for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int kv = kv0 + 32 * mb + 8 * (r >> 2) + 4 * h + (r & 3);
-                        const bool dead = (CAUSAL && kv > qrow) || kv >= S;
-                        sacc[mb][r] = dead ? -INFINITY : sacc[mb][r];
-                    }
-            }
-            // row max over this lane's 32 keys, then across the two half-waves
-            float mx = sacc[0][0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][r]);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][r]);
-            mx = max_halves(mx);
-            const float m_new = mx * c;
-            const bool need = m_new > m_ref + tau;
-            if (__builtin_amdgcn_ballot_w64(need)) {
-                const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
-                m_ref = need ? m_new : m_ref;
-                l_sum *= alpha;
-#pragma unroll
-                for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
-            }
-            const float nm = -m_ref;
-            // P = 2^(s c - m_ref); pack to bf16 in MFMA k order; partial row sum
-            fa_u32x4 pf[4];
-            float lpart = 0.0f;
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    const float p0 = exp2_sel<POLY, DEG>(fmaf(sacc[mb][r], c, nm), r);
-                    const float p1 = exp2_sel<POLY, DEG>(fmaf(sacc[mb][r + 1], c, nm), r + 1);
-                    lpart += p0 + p1;
-                    pf[2 * mb + (r >> 3)][(r & 7) >> 1] = pack_bf16(p0, p1);
-                }
-            }
-            l_sum += lpart;
-            // O^T += V^T P^T, k-step t covers keys 16t .. 16t+15 of the tile in
-            // accumulator order; V^T operand by transposing reads of V rows.
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int rbase = 16 * t + 4 * h;  // = 32 mb + 16 t' + 4h
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const fa_u32x4 a = operand_tr<NCH>(sV, rbase, rbase + 8, 32 * db, lane);
-                    oacc[db] = mfma32(a, pf[t], oacc[db]);
-                }
-            }
-        }
-        wait_vmem();      // tile j+1 has landed in the other buffer
-        __syncthreads();  // ... for every wave, and nobody still reads this one
-    }
+    const int n_plain = min(nkv, (CAUSAL ? min(q0, S) : S) / kBc);
+    for (int j = 0; j < n_plain; ++j) step(j, std::false_type{});
+    for (int j = n_plain; j < nkv; ++j) step(j, std::true_type{});
 
     // Epilogue: join the half-row sums, normalise, store O (bf16) and LSE.
     const float l_tot = sum_halves(l_sum);

@@ -25,7 +25,7 @@ struct BwdArgs {
     const float *LSE;
     float *dQ;
     void *dK, *dV;
-    float *Dvec;  // workspace, BH*S floats
+    float *Dvec;  // workspace: D (BH*S floats), then LSE*log2(e) (BH*S floats)
     int BH, S, d;
     float scale;
     bool causal;

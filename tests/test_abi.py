@@ -76,23 +76,24 @@ def test_empty_calls_are_ok_without_gpu(lib):
 
 
 def test_backward_checks(lib):
-    assert lib.fa_bwd_workspace_bytes(2, 3, 100, 128) == 2 * 3 * 100 * 4
+    assert lib.fa_bwd_workspace_bytes(2, 3, 100, 128) == 2 * 2 * 3 * 100 * 4
     p9 = [A] * 9
-    # workspace too small
-    assert lib.fa_bwd(*p9, 1, 1, 128, 128, ctypes.c_float(0.1), 0, A, 4, NULL) == 1
+    # workspace too small (needs 2 * 128 floats)
+    assert lib.fa_bwd(*p9, 1, 1, 128, 128, ctypes.c_float(0.1), 0, A, 1020, NULL) == 1
     # null workspace
-    assert lib.fa_bwd(*p9, 1, 1, 128, 128, ctypes.c_float(0.1), 0, NULL, 512, NULL) == 1
+    assert lib.fa_bwd(*p9, 1, 1, 128, 128, ctypes.c_float(0.1), 0, NULL, 1024, NULL) == 1
     # misaligned dQ
     p = list(p9)
     p[6] = MIS
-    assert lib.fa_bwd(*p, 1, 1, 128, 128, ctypes.c_float(0.1), 0, A, 512, NULL) == 1
-    assert lib.fa_bwd(*p9, 1, 1, 128, 64 + 1, ctypes.c_float(0.1), 0, A, 512, NULL) == 2
-    assert lib.fa_bwd_dkdv(*([A] * 7), 1, 1, 128, 128, ctypes.c_float(0.1), 3, A, 512, NULL) == 1
-    assert lib.fa_bwd_dkdv(*([A] * 6), MIS, 1, 1, 128, 128, ctypes.c_float(0.1), 0, A, 512, NULL) == 1
-    assert lib.fa_bwd_dq(*([A] * 5), MIS, 1, 1, 128, 128, ctypes.c_float(0.1), 0, A, 512, NULL) == 1
-    assert lib.fa_bwd_dq(*([A] * 6), 1, 1, 128, 128, ctypes.c_float(0.0), 0, A, 512, NULL) == 1
-    assert lib.fa_bwd_preprocess(A, MIS, 1, 1, 128, 128, A, 512, NULL) == 1
-    assert lib.fa_bwd_preprocess(A, A, 1, 1, 128, 128, A, 4, NULL) == 1
+    assert lib.fa_bwd(*p, 1, 1, 128, 128, ctypes.c_float(0.1), 0, A, 1024, NULL) == 1
+    assert lib.fa_bwd(*p9, 1, 1, 128, 64 + 1, ctypes.c_float(0.1), 0, A, 1024, NULL) == 2
+    assert lib.fa_bwd_dkdv(*([A] * 6), 1, 1, 128, 128, ctypes.c_float(0.1), 3, A, 1024, NULL) == 1
+    assert lib.fa_bwd_dkdv(*([A] * 5), MIS, 1, 1, 128, 128, ctypes.c_float(0.1), 0, A, 1024, NULL) == 1
+    assert lib.fa_bwd_dq(*([A] * 4), MIS, 1, 1, 128, 128, ctypes.c_float(0.1), 0, A, 1024, NULL) == 1
+    assert lib.fa_bwd_dq(*([A] * 5), 1, 1, 128, 128, ctypes.c_float(0.0), 0, A, 1024, NULL) == 1
+    assert lib.fa_bwd_preprocess(A, MIS, A, 1, 1, 128, 128, A, 1024, NULL) == 1
+    assert lib.fa_bwd_preprocess(A, A, NULL, 1, 1, 128, 128, A, 1024, NULL) == 1
+    assert lib.fa_bwd_preprocess(A, A, A, 1, 1, 128, 128, A, 4, NULL) == 1
 
 
 def test_softmax_options_validation(lib):

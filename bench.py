@@ -89,6 +89,71 @@ def cpu_baseline(bits, S, d, scale, rows_n=2048):
                       f"(the dQ-rows routine does 8*S*d of the 10*S*d, so the CPU figure is flattered)"}
 
 
+def _time(fn, reps=5):
+    """Mean milliseconds of fn() over reps launches (events on the current stream)."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def ablation(fa, gen, dev, q, k, v, do, B, H, S, d, scale):
+    """One JSON line: kernel times under each softmax option and causal order."""
+    import torch
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+    dq = torch.empty((B, H, S, d), dtype=torch.float32, device="cuda")
+    dk, dv = torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, S, d) // 4, dtype=torch.float32, device="cuda")
+    rows = []
+    for tau, poly, deg in [(8.0, 0, 3), (0.0, 0, 3), (8.0, 1, 3), (8.0, 2, 3), (8.0, 1, 5), (8.0, 2, 5)]:
+        fa.fa_set_softmax_options(tau, poly, deg)
+        for causal in (False, True):
+            ms = _time(lambda: fa.fa_fwd(q, k, v, o, lse, scale, causal))
+            fl = flops(B, H, S, d, causal, False)
+            rows.append({"kernel": "fwd", "workload": WORKLOAD, "causal": causal, "tau": tau,
+                         "poly_eighths": poly, "poly_degree": deg, "ms": round(ms, 4),
+                         "tflops": round(fl / ms / 1e9, 1)})
+    fa.fa_set_softmax_options(8.0, 0, 3)
+    # rescale threshold on the workload built to move the running max
+    wname = "causal_boost_b2_h16_s8192"
+    w = gen.WORKLOADS[wname]
+    bb = gen.workload_inputs(wname, ("q", "k", "v"))
+    qb, kb, vb = (dev(bb[t]) for t in "qkv")
+    ob = torch.empty_like(qb)
+    lb = torch.empty(qb.shape[:3], dtype=torch.float32, device="cuda")
+    sb = gen.default_scale(w["d"])
+    for tau in (0.0, 2.0, 8.0):
+        fa.fa_set_softmax_options(tau, 0, 3)
+        ms = _time(lambda: fa.fa_fwd(qb, kb, vb, ob, lb, sb, True))
+        fl = flops(w["B"], w["H"], w["S"], w["d"], True, False)
+        rows.append({"kernel": "fwd", "workload": wname, "causal": True, "tau": tau, "poly_eighths": 0,
+                     "poly_degree": 3, "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1)})
+    fa.fa_set_softmax_options(8.0, 0, 3)
+    # causal block order: longest first (LPT) vs shortest first
+    fa.fa_fwd(q, k, v, o, lse, scale, True)
+    fa.fa_bwd_preprocess(o, do, lse, ws)
+    for lpt in (True, False):
+        fa.fa_set_causal_order(lpt)
+        for name, fn, fl in (
+                ("fwd", lambda: fa.fa_fwd(q, k, v, o, lse, scale, True), flops(B, H, S, d, True, False)),
+                ("bwd_dkdv", lambda: fa.fa_bwd_dkdv(q, k, v, do, dk, dv, scale, True, ws),
+                 0.8 * flops(B, H, S, d, True, True)),
+                ("bwd_dq", lambda: fa.fa_bwd_dq(q, k, v, do, dq, scale, True, ws),
+                 0.2 * flops(B, H, S, d, True, True))):
+            ms = _time(fn)
+            rows.append({"kernel": name, "workload": WORKLOAD, "causal": True, "longest_first": lpt,
+                         "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1)})
+    fa.fa_set_causal_order(True)
+    print(json.dumps({"ablation": rows}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -96,6 +161,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=24576)
+    ap.add_argument("--ablation", action="store_true",
+                    help="time the softmax options (hybrid exp share, polynomial degree, rescale "
+                         "threshold) and the causal block order instead of the step")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: this build measures one MI355X "
@@ -121,6 +189,9 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda()
 
     q, k, v, do = (dev(bits[t]) for t in ("q", "k", "v", "do"))
+    if args.ablation:
+        ablation(fa, gen, dev, q, k, v, do, B, H, S, d, scale)
+        return
     o = torch.empty_like(q)
     lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
     dq = torch.empty((B, H, S, d), dtype=torch.float32, device="cuda")

@@ -53,6 +53,8 @@ def load_library():
     lib.fa_bwd_dq.restype = i
     lib.fa_set_softmax_options.argtypes = [f, i, i]
     lib.fa_set_softmax_options.restype = i
+    lib.fa_set_causal_order.argtypes = [i]
+    lib.fa_set_causal_order.restype = i
     lib.fa_exp2_poly.argtypes = [vp, vp, ctypes.c_int64, i, vp]
     lib.fa_exp2_poly.restype = i
     _lib = lib
@@ -178,6 +180,10 @@ def fa_bwd_dq(q, k, v, do, dq, scale: float, causal: bool, workspace, stream=Non
 def fa_set_softmax_options(rescale_tau: float = 8.0, poly_eighths: int = 0, poly_degree: int = 3):
     _check(load_library().fa_set_softmax_options(float(rescale_tau), int(poly_eighths), int(poly_degree)),
            "fa_set_softmax_options")
+
+
+def fa_set_causal_order(longest_first: bool = True):
+    _check(load_library().fa_set_causal_order(int(bool(longest_first))), "fa_set_causal_order")
 
 
 def fa_exp2_poly(x, y, degree: int = 3, stream=None):

@@ -16,6 +16,7 @@ namespace {
 std::atomic<float> g_tau{8.0f};
 std::atomic<int> g_poly_eighths{0};
 std::atomic<int> g_poly_degree{3};
+std::atomic<int> g_lpt{1};
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -75,6 +76,12 @@ fa_status fa_set_softmax_options(float rescale_tau, int poly_eighths, int poly_d
     return FA_OK;
 }
 
+fa_status fa_set_causal_order(int longest_first) {
+    if (longest_first != 0 && longest_first != 1) return FA_ERR_INVALID;
+    g_lpt.store(longest_first);
+    return FA_OK;
+}
+
 fa_status fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE, int B, int H,
                  int S, int d, float scale, int causal, void *stream) {
     bool empty = false;
@@ -86,7 +93,7 @@ fa_status fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LS
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
         return FA_ERR_INVALID;
     fa::FwdArgs a{Q, K, V, O, LSE, B * H, S, d, scale, causal == 1,
-                  g_tau.load(), g_poly_eighths.load(), g_poly_degree.load()};
+                  g_tau.load(), g_poly_eighths.load(), g_poly_degree.load(), g_lpt.load() != 0};
     return hip_status(fa::launch_fwd(a, (hipStream_t)stream));
 }
 
@@ -146,6 +153,7 @@ static fa_status bwd_grad_args(const void *Q, const void *K, const void *V,
     a->d = d;
     a->scale = scale;
     a->causal = causal == 1;
+    a->lpt = g_lpt.load() != 0;
     return FA_OK;
 }
 

@@ -94,7 +94,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const float *__restrict__ L2vec, const float *__restrict__ Dvec, const uint16_t *__restrict__ dO,
-    uint16_t *__restrict__ dK, uint16_t *__restrict__ dV, int BH, int S, float scale, float c) {
+    uint16_t *__restrict__ dK, uint16_t *__restrict__ dV, int BH, int S, float scale, float c, int lpt) {
     constexpr int NW = 8;
     constexpr int ROWB = D * 2;
     constexpr int NCH = ROWB / 16;
@@ -119,7 +119,10 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
     const int qh = w >> 2;  // query half of this wave
 
     const int bh = blockIdx.x % BH;
-    const int kblk = blockIdx.x / BH;
+    // causal: key block 0 meets the most query blocks, so ascending ids run
+    // longest first; lpt == 0 reverses the order (for measurement)
+    const int kblk = (CAUSAL && !lpt) ? ((S + kKvPerBlock - 1) / kKvPerBlock - 1 - (int)(blockIdx.x / BH))
+                                      : (int)(blockIdx.x / BH);
     const int k0 = kblk * kKvPerBlock;
     const size_t head = (size_t)bh * (size_t)S * D;
     const int kv = k0 + 32 * kw + n;  // this lane's key for S and dP
@@ -290,7 +293,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const float *__restrict__ L2vec, const float *__restrict__ Dvec, const uint16_t *__restrict__ dO,
-    float *__restrict__ dQ, int BH, int S, float scale, float c, int nqb) {
+    float *__restrict__ dQ, int BH, int S, float scale, float c, int nqb, int lpt) {
     constexpr int ROWB = D * 2;
     constexpr int NCH = ROWB / 16;
     constexpr int KS = D / 16;
@@ -305,7 +308,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 
     const int bh = blockIdx.x % BH;
     const int qi = blockIdx.x / BH;
-    const int qblk = CAUSAL ? (nqb - 1 - qi) : qi;
+    const int qblk = (CAUSAL && lpt) ? (nqb - 1 - qi) : qi;
     const int q0 = qblk * kQPerBlock;
     const size_t head = (size_t)bh * (size_t)S * D;
     const int kv_end = CAUSAL ? min(S, q0 + kQPerBlock) : S;
@@ -454,7 +457,7 @@ hipError_t launch_dkdv_t(const BwdArgs &a, hipStream_t st) {
                        (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
                        (const float *)a.Dvec + (size_t)a.BH * a.S, (const float *)a.Dvec,
                        (const uint16_t *)a.dO, (uint16_t *)a.dK, (uint16_t *)a.dV,
-                       a.BH, a.S, a.scale, a.scale * FA_LOG2E);
+                       a.BH, a.S, a.scale, a.scale * FA_LOG2E, (int)a.lpt);
     return hipGetLastError();
 }
 
@@ -465,7 +468,7 @@ hipError_t launch_dq_t(const BwdArgs &a, hipStream_t st) {
                        (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
                        (const float *)a.Dvec + (size_t)a.BH * a.S, (const float *)a.Dvec,
                        (const uint16_t *)a.dO, a.dQ, a.BH, a.S, a.scale,
-                       a.scale * FA_LOG2E, nqb);
+                       a.scale * FA_LOG2E, nqb, (int)a.lpt);
     return hipGetLastError();
 }
 

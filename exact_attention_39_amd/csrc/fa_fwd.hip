@@ -59,7 +59,8 @@ __device__ __forceinline__ float exp2_sel(float x, int r) {
 template <int D, bool CAUSAL, int POLY, int DEG>
 __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
-    uint16_t *__restrict__ O, float *__restrict__ LSE, int BH, int S, float c, float tau, int nqb) {
+    uint16_t *__restrict__ O, float *__restrict__ LSE, int BH, int S, float c, float tau, int nqb,
+    int lpt) {
     constexpr int ROWB = D * 2;        // bytes per row
     constexpr int NCH = ROWB / 16;     // 16-byte chunks per row
     constexpr int KS = D / 16;         // k-steps over d
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(
 
     const int bh = blockIdx.x % BH;
     const int qi = blockIdx.x / BH;
-    const int qblk = CAUSAL ? (nqb - 1 - qi) : qi;
+    const int qblk = (CAUSAL && lpt) ? (nqb - 1 - qi) : qi;
     const int q0 = qblk * kBr;
     const size_t head = (size_t)bh * (size_t)S * D;
     const int kv_end = CAUSAL ? min(S, q0 + kBr) : S;
@@ -252,7 +253,7 @@ hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t st) {
     const dim3 grid((unsigned)(a.BH * nqb)), block(kFwdThreads);
     hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, POLY, DEG>), grid, block, 0, st,
                        (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
-                       (uint16_t *)a.O, a.LSE, a.BH, a.S, a.scale * FA_LOG2E, a.tau, nqb);
+                       (uint16_t *)a.O, a.LSE, a.BH, a.S, a.scale * FA_LOG2E, a.tau, nqb, (int)a.lpt);
     return hipGetLastError();
 }
 

@@ -18,6 +18,7 @@ struct FwdArgs {
     float tau;         // rescale threshold, log2 units
     int poly_eighths;  // 0, 1 or 2
     int poly_degree;   // 3 or 5
+    bool lpt;          // causal: longest query blocks first
 };
 
 struct BwdArgs {
@@ -29,6 +30,7 @@ struct BwdArgs {
     int BH, S, d;
     float scale;
     bool causal;
+    bool lpt;     // causal: longest blocks first
 };
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t st);

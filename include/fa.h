@@ -139,6 +139,16 @@ fa_status fa_bwd_dq(const void *Q, const void *K, const void *V,
 fa_status fa_set_softmax_options(float rescale_tau, int poly_eighths, int poly_degree);
 
 /*
+ * Causal block order, process-wide like the softmax options.  1 (default):
+ * longest blocks first -- the LPT order of the technical summary's results
+ * (forward and dQ kernel: last query blocks first; dK/dV kernel: first key
+ * blocks first).  0: the reverse, shortest first, kept for measuring what
+ * the order is worth.  The result does not depend on it.  Returns
+ * FA_ERR_INVALID for other values.
+ */
+fa_status fa_set_causal_order(int longest_first);
+
+/*
  * Diagnostic: y[i] = exp2 of x[i] through the device polynomial of the given
  * degree (3 or 5), as the forward kernel evaluates it.  x, y: device fp32
  * arrays of n elements.  For x < -126 the result is 0; the polynomial is

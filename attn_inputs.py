@@ -30,7 +30,7 @@ GOLDEN = np.uint64(0x9E3779B97F4A7C15)
 M1 = np.uint64(0xBF58476D1CE4E5B9)
 M2 = np.uint64(0x94D049BB133111EB)
 
-TENSOR_ID = {"q": 0, "k": 1, "v": 2, "do": 3}
+TENSOR_ID = {"q": 0, "k": 1, "v": 2, "do": 3, "lengths": 15}
 
 # Workloads of the attention pages' evaluation, with the shapes they are
 # quoted on.  ``id`` feeds the seed.  ``boost`` = (period, factor): every
@@ -133,6 +133,31 @@ def workload_inputs(name: str, tensors=("q", "k", "v", "do"), S=None, B=None, H=
     w = WORKLOADS[name]
     shape = (B or w["B"], H or w["H"], S or w["S"], w["d"])
     return {t: make_tensor_bf16(w["id"], t, shape, w["boost"]) for t in tensors}
+
+
+# Packed variable-length prefill batches (forward only, causal): n sequence
+# lengths, each `unit` times a SplitMix64 draw uniform in 1..max_units, so a
+# mix of short and long prompts; tensors are [total, H, d] (token-major).
+VARLEN_WORKLOADS = {
+    "prefill_varlen_h16_d128": dict(id=6, n=16, unit=128, max_units=128, H=16, d=128, causal=True),
+}
+
+
+def varlen_lengths(name: str) -> np.ndarray:
+    w = VARLEN_WORKLOADS[name]
+    u = splitmix64(seed_for(w["id"], "lengths"), 0, w["n"])
+    return (w["unit"] * (1 + (u % np.uint64(w["max_units"])))).astype(np.int64)
+
+
+def varlen_inputs(name: str, tensors=("q", "k", "v")):
+    """(lengths, bf16 bits [total, H, d] per tensor) for the named batch."""
+    w = VARLEN_WORKLOADS[name]
+    lens = varlen_lengths(name)
+    total = int(lens.sum())
+    shape = (total, w["H"], w["d"])
+    bits = {t: f32_to_bf16_bits(normal_f32(seed_for(w["id"], t), total * w["H"] * w["d"]).reshape(shape))
+            for t in tensors}
+    return lens, bits
 
 
 def default_scale(d: int) -> float:

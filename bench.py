@@ -154,6 +154,52 @@ def ablation(fa, gen, dev, q, k, v, do, B, H, S, d, scale):
     print(json.dumps({"ablation": rows}), flush=True)
 
 
+def varlen_bench(fa, gen, args, name="prefill_varlen_h16_d128"):
+    """Forward-only prefill over a packed batch of causal sequences of mixed
+    lengths: TFLOPS = sum over sequences of 2 * H * L^2 * d (the causal half
+    of 4 * H * L^2 * d) / mean time of one fa_fwd_varlen call."""
+    import numpy as np
+    import torch
+
+    w = gen.VARLEN_WORKLOADS[name]
+    print(f"[bench] generating inputs {name}", file=sys.stderr, flush=True)
+    lens, bits = gen.varlen_inputs(name)
+    H, d = w["H"], w["d"]
+    total = int(lens.sum())
+    scale = gen.default_scale(d)
+
+    def dev(b):
+        return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda()
+
+    q, k, v = (dev(bits[t]) for t in ("q", "k", "v"))
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((H, total), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    maxlen = int(lens.max())
+    call = lambda: fa.fa_fwd_varlen(q, k, v, o, lse, cu, maxlen, scale, w["causal"], stream)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    fl = float(sum(4.0 * H * float(L) ** 2 * d * (0.5 if w["causal"] else 1.0) for L in lens))
+    tf = fl / (ms / 1e3) / 1e12
+    print(json.dumps({
+        "metric": "prefill forward TFLOPS, packed variable-length causal batch, bf16 d=128",
+        "value": round(tf, 1), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 3), "higher_is_better": True, "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic", "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+        "config": {"workload": name, "nseq": int(len(lens)), "total_tokens": total, "H": H, "d": d,
+                   "min_len": int(lens.min()), "max_len": maxlen, "causal": w["causal"]},
+    }))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -161,6 +207,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=24576)
+    ap.add_argument("--varlen", action="store_true",
+                    help="time the packed variable-length prefill forward (fa_fwd_varlen) on the "
+                         "prefill_varlen_h16_d128 batch instead of the step; prints its own JSON line")
     ap.add_argument("--ablation", action="store_true",
                     help="time the softmax options (hybrid exp share, polynomial degree, rescale "
                          "threshold) and the causal block order instead of the step")
@@ -179,6 +228,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     fa.load_library()
     fa.fa_set_softmax_options(8.0, 0, 3)
+    if args.varlen:
+        varlen_bench(fa, gen, args)
+        return
     w = gen.WORKLOADS[WORKLOAD]
     B, H, S, d = w["B"], w["H"], w["S"], w["d"]
     scale = gen.default_scale(d)

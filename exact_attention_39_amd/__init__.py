@@ -41,6 +41,8 @@ def load_library():
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
     lib.fa_fwd.restype = i
+    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd_varlen.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
@@ -109,6 +111,25 @@ def fa_fwd(q, k, v, o, lse, scale: float, causal: bool, stream=None):
     _check_tensor(lse, "lse", torch.float32, (B, H, S))
     _check(load_library().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, S, d,
                                  float(scale), int(bool(causal)), _stream(stream)), "fa_fwd")
+
+
+def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, max_seqlen: int, scale: float, causal: bool, stream=None):
+    """Packed variable-length forward: q, k, v, o bf16 [total, H, d]; lse fp32
+    [H, total]; cu_seqlens int32 [nseq + 1] on the GPU."""
+    import torch
+    if q.dim() != 3:
+        raise ValueError("q must be [total, H, d]")
+    total, H, d = (int(x) for x in q.shape)
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _check_tensor(t, nm, torch.bfloat16, (total, H, d))
+    _check_tensor(lse, "lse", torch.float32, (H, total))
+    if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D tensor of nseq + 1 offsets")
+    _check_tensor(cu_seqlens, "cu_seqlens", torch.int32, tuple(cu_seqlens.shape))
+    nseq = cu_seqlens.numel() - 1
+    _check(load_library().fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens),
+                                        nseq, H, total, int(max_seqlen), d, float(scale),
+                                        int(bool(causal)), _stream(stream)), "fa_fwd_varlen")
 
 
 def fa_bwd_workspace_bytes(B: int, H: int, S: int, d: int) -> int:
@@ -203,6 +224,19 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, stream=No
     o = torch.empty_like(q)
     lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     fa_fwd(q, k, v, o, lse, scale, causal, stream)
+    return o, lse
+
+
+def forward_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False, scale: float | None = None,
+                   stream=None):
+    """(O bf16 [total, H, d], LSE fp32 [H, total]) for a packed batch of
+    sequences delimited by cu_seqlens (int32 [nseq + 1] on the GPU)."""
+    import torch
+    total, H, d = (int(x) for x in q.shape)
+    scale = d ** -0.5 if scale is None else scale
+    o = torch.empty_like(q)
+    lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, max_seqlen, scale, causal, stream)
     return o, lse
 
 

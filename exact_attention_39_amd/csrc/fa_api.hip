@@ -97,6 +97,30 @@ fa_status fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LS
     return hip_status(fa::launch_fwd(a, (hipStream_t)stream));
 }
 
+fa_status fa_fwd_varlen(const void *Q, const void *K, const void *V, void *O, float *LSE,
+                        const int *cu_seqlens, int nseq, int H, int total, int max_seqlen, int d,
+                        float scale, int causal, void *stream) {
+    if (nseq < 0 || H < 0 || total < 0 || max_seqlen < 0) return FA_ERR_INVALID;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (!good_scale(scale) || (causal != 0 && causal != 1)) return FA_ERR_INVALID;
+    if (max_seqlen > (1 << 22)) return FA_ERR_INVALID;
+    // byte offsets inside one (sequence, head) stay 32-bit: total * H * d * 2 < 2^32
+    if ((int64_t)total * H * d * 2 >= ((int64_t)1 << 32)) return FA_ERR_INVALID;
+    const int64_t units = (int64_t)nseq * H;
+    if (units > INT32_MAX || units * (((int64_t)max_seqlen + 63) / 64) > INT32_MAX) return FA_ERR_INVALID;
+    if (units == 0 || total == 0 || max_seqlen == 0) return FA_OK;
+    if (!Q || !K || !V || !O || !LSE || !cu_seqlens) return FA_ERR_INVALID;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE) ||
+        ((uintptr_t)cu_seqlens & 3u) != 0)
+        return FA_ERR_INVALID;
+    fa::FwdArgs a{Q, K, V, O, LSE, (int)units, max_seqlen, d, scale, causal == 1,
+                  g_tau.load(), g_poly_eighths.load(), g_poly_degree.load(), g_lpt.load() != 0};
+    a.cu_seqlens = cu_seqlens;
+    a.H = H;
+    a.total = total;
+    return hip_status(fa::launch_fwd(a, (hipStream_t)stream));
+}
+
 size_t fa_bwd_workspace_bytes(int B, int H, int S, int d) {
     (void)d;
     if (B <= 0 || H <= 0 || S <= 0) return 0;

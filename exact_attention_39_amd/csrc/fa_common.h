@@ -132,15 +132,16 @@ __device__ __forceinline__ int swz(int row) {
     }
 }
 
-// Copy ROWS rows of a row-major global matrix (row pitch NCH*16 bytes,
-// starting at byte offset row0 * pitch of the resource) into a swizzled LDS
-// tile with NW waves (w = wave index, wave-uniform), straight from memory to
-// LDS.  Each wave instruction fills 1 KB of LDS contiguously, so the swizzle
-// is applied on the global side: the lane that owns physical chunk pc of a
-// row fetches logical chunk pc ^ swz(row).  Rows past the resource end
-// arrive as zeros.
+// Copy ROWS rows of a row-major global matrix (rows of NCH*16 bytes, PITCH
+// bytes apart, starting at byte offset row0 * PITCH of the resource) into a
+// swizzled LDS tile with NW waves (w = wave index, wave-uniform), straight
+// from memory to LDS.  Each wave instruction fills 1 KB of LDS contiguously,
+// so the swizzle is applied on the global side: the lane that owns physical
+// chunk pc of a row fetches logical chunk pc ^ swz(row).  Rows past the
+// resource end arrive as zeros.
 template <int NCH, int ROWS, int NW = 4>
-__device__ __forceinline__ void tile_to_lds(fa_rsrc r, int row0, fa_lds_char *tile, int w, int lane) {
+__device__ __forceinline__ void tile_to_lds_pitched(fa_rsrc r, int row0, uint32_t pitch,
+                                                    fa_lds_char *tile, int w, int lane) {
     constexpr int ROWB = NCH * 16;
     constexpr int ROWS_PER_INST = 1024 / ROWB;
     constexpr int INSTS = ROWS * ROWB / 1024;   // wave instructions for the tile
@@ -151,9 +152,15 @@ __device__ __forceinline__ void tile_to_lds(fa_rsrc r, int row0, fa_lds_char *ti
         const int row = inst * ROWS_PER_INST + lane / NCH;
         const int pc = lane % NCH;
         const int c = pc ^ swz<NCH>(row);
-        const uint32_t goff = (uint32_t)(row0 + row) * ROWB + c * 16;
+        const uint32_t goff = (uint32_t)(row0 + row) * pitch + c * 16;
         buf_load_lds<16>(r, tile + inst * 1024, goff);
     }
+}
+
+// The same for densely packed rows (pitch = row length).
+template <int NCH, int ROWS, int NW = 4>
+__device__ __forceinline__ void tile_to_lds(fa_rsrc r, int row0, fa_lds_char *tile, int w, int lane) {
+    tile_to_lds_pitched<NCH, ROWS, NW>(r, row0, NCH * 16, tile, w, lane);
 }
 
 // Byte offset of (row, byte-in-row) inside a swizzled tile with NCH chunks per row.

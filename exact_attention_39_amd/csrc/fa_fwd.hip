@@ -56,11 +56,17 @@ __device__ __forceinline__ float exp2_sel(float x, int r) {
     return __builtin_amdgcn_exp2f(x);
 }
 
-template <int D, bool CAUSAL, int POLY, int DEG>
+// VARLEN: packed variable-length batch.  Workgroup (unit u, block qi) with
+// u = blockIdx % BH takes sequence u / H, head u % H; its rows are tokens
+// cu[s] .. cu[s+1]-1 of a [total][H][D] tensor (row pitch H * D elements),
+// LSE is [H][total].  cu entries are clamped to [0, total] and made
+// non-decreasing, so no access leaves the tensors whatever they hold.
+// Otherwise unit u is head u of a [BH][S][D] tensor, LSE [BH][S].
+template <int D, bool CAUSAL, int POLY, int DEG, bool VARLEN>
 __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
-    uint16_t *__restrict__ O, float *__restrict__ LSE, int BH, int S, float c, float tau, int nqb,
-    int lpt) {
+    uint16_t *__restrict__ O, float *__restrict__ LSE, int BH, int S_arg, float c, float tau, int nqb,
+    int lpt, const int *__restrict__ cu, int H, int total) {
     constexpr int ROWB = D * 2;        // bytes per row
     constexpr int NCH = ROWB / 16;     // 16-byte chunks per row
     constexpr int KS = D / 16;         // k-steps over d
@@ -77,16 +83,34 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(
     const int qi = blockIdx.x / BH;
     const int qblk = (CAUSAL && lpt) ? (nqb - 1 - qi) : qi;
     const int q0 = qblk * kBr;
-    const size_t head = (size_t)bh * (size_t)S * D;
+    int S;                // rows of this unit
+    size_t head;          // element offset of its row 0
+    size_t lse0;          // index of its row 0 in LSE
+    uint32_t pitch;       // bytes between consecutive rows
+    if constexpr (VARLEN) {
+        const int seq = bh / H, hh = bh - seq * H;
+        const int start = min(max(cu[seq], 0), total);
+        const int end = min(max(cu[seq + 1], start), total);
+        S = end - start;
+        if (q0 >= S) return;  // whole workgroup, before any barrier
+        head = ((size_t)start * H + hh) * D;
+        lse0 = (size_t)hh * total + start;
+        pitch = (uint32_t)H * ROWB;
+    } else {
+        S = S_arg;
+        head = (size_t)bh * (size_t)S * D;
+        lse0 = (size_t)bh * S;
+        pitch = ROWB;
+    }
     const int kv_end = CAUSAL ? min(S, q0 + kBr) : S;
     const int nkv = (kv_end + kBc - 1) / kBc;
 
     const int qrow = q0 + 32 * w + n;   // this lane's query row
     const int wq_lo = q0 + 32 * w;      // first query row of the wave
 
-    // Per-head buffer resources: rows at or past S read as zero and are
-    // never written.
-    const uint32_t head_bytes = (uint32_t)S * ROWB;
+    // Per-unit buffer resources end with row S - 1: rows at or past S read
+    // as zero and are never written.
+    const uint32_t head_bytes = (uint32_t)(S - 1) * pitch + ROWB;
     const fa_rsrc rQ = make_rsrc(Q + head, head_bytes);
     const fa_rsrc rK = make_rsrc(K + head, head_bytes);
     const fa_rsrc rV = make_rsrc(V + head, head_bytes);
@@ -94,7 +118,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(
     // Q^T as the B operand of S^T = K Q^T: lane holds Q[qrow][16ks + 8h .. +7].
     fa_u32x4 qf[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = buf_load16(rQ, (uint32_t)qrow * ROWB + (16 * ks + 8 * h) * 2);
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = buf_load16(rQ, (uint32_t)qrow * pitch + (16 * ks + 8 * h) * 2);
 
     fa_f32x16 oacc[DB];
 #pragma unroll
@@ -104,8 +128,8 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(
 
     auto issue_tile = [&](int j, int buf) {
         fa_lds_char *sK = smem + buf * 2 * TILE;
-        tile_to_lds<NCH, kBc>(rK, j * kBc, sK, w, lane);
-        tile_to_lds<NCH, kBc>(rV, j * kBc, sK + TILE, w, lane);
+        tile_to_lds_pitched<NCH, kBc>(rK, j * kBc, pitch, sK, w, lane);
+        tile_to_lds_pitched<NCH, kBc>(rV, j * kBc, pitch, sK + TILE, w, lane);
     };
 
     // Lane-dependent LDS offsets, computed once.  Row reads of key row
@@ -239,10 +263,10 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(
         for (int g = 0; g < 4; ++g) {
             fa_u32x2 v = {pack_bf16(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
                           pack_bf16(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
-            buf_store8(rO, (uint32_t)qrow * ROWB + (32 * db + 8 * g + 4 * h) * 2, v);
+            buf_store8(rO, (uint32_t)qrow * pitch + (32 * db + 8 * g + 4 * h) * 2, v);
         }
     if (h == 0) {
-        const fa_rsrc rL = make_rsrc(LSE + (size_t)bh * S, (uint32_t)S * 4);
+        const fa_rsrc rL = make_rsrc(LSE + lse0, (uint32_t)S * 4);
         buf_store4(rL, (uint32_t)qrow * 4, __float_as_uint((m_ref + __log2f(l_tot)) * FA_LN2));
     }
 }
@@ -251,9 +275,16 @@ template <int D, bool CAUSAL, int POLY, int DEG>
 hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t st) {
     const int nqb = (a.S + kBr - 1) / kBr;
     const dim3 grid((unsigned)(a.BH * nqb)), block(kFwdThreads);
-    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, POLY, DEG>), grid, block, 0, st,
-                       (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
-                       (uint16_t *)a.O, a.LSE, a.BH, a.S, a.scale * FA_LOG2E, a.tau, nqb, (int)a.lpt);
+    if (a.cu_seqlens)
+        hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, POLY, DEG, true>), grid, block, 0, st,
+                           (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
+                           (uint16_t *)a.O, a.LSE, a.BH, a.S, a.scale * FA_LOG2E, a.tau, nqb, (int)a.lpt,
+                           a.cu_seqlens, a.H, a.total);
+    else
+        hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, POLY, DEG, false>), grid, block, 0, st,
+                           (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
+                           (uint16_t *)a.O, a.LSE, a.BH, a.S, a.scale * FA_LOG2E, a.tau, nqb, (int)a.lpt,
+                           (const int *)nullptr, 0, 0);
     return hipGetLastError();
 }
 

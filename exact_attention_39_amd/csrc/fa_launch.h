@@ -19,6 +19,13 @@ struct FwdArgs {
     int poly_eighths;  // 0, 1 or 2
     int poly_degree;   // 3 or 5
     bool lpt;          // causal: longest query blocks first
+    // Packed variable-length batch (cu_seqlens != nullptr): nseq sequences,
+    // sequence s = tokens cu_seqlens[s] .. cu_seqlens[s+1]-1 of Q, K, V, O
+    // laid out [total][H][d]; LSE [H][total].  BH = nseq * H and S =
+    // max_seqlen then.
+    const int *cu_seqlens = nullptr;
+    int H = 0;
+    int total = 0;
 };
 
 struct BwdArgs {

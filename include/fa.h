@@ -74,6 +74,30 @@ const char *fa_status_string(fa_status s);
 fa_status fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE,
                  int B, int H, int S, int d, float scale, int causal, void *stream);
 
+/*
+ * Forward pass over a packed batch of variable-length sequences (the
+ * forward-only prefill case; the pages' kernel serves prefill in inference
+ * engines, hyper.ai story).  Sequence s (0 <= s < nseq) is tokens
+ * cu_seqlens[s] .. cu_seqlens[s+1]-1; attention never crosses sequences,
+ * and under causal = 1 token i of a sequence sees its tokens 0 .. i.
+ *   Q, K, V, O: bf16 [total][H][d] (token-major, heads interleaved), device.
+ *   LSE: fp32 [H][total], device.
+ *   cu_seqlens: device int32 array of nseq + 1 offsets, 4-byte aligned,
+ *     expected non-decreasing from 0 to total.  The kernel clamps every
+ *     entry to [0, total] and to at least the previous one, so bad offsets
+ *     cannot make it touch memory outside the tensors; tokens covered by no
+ *     sequence are not written.
+ *   max_seqlen: an upper bound of the sequence lengths (the launch covers
+ *     this many rows per sequence; rows of a longer sequence past it are
+ *     not written).
+ * total * H * d * 2 must stay below 2^32, max_seqlen <= 2^22.  nseq, H,
+ * total or max_seqlen equal to 0 is a valid empty call.  Other rules as
+ * fa_fwd.  Uses the same softmax options and causal order as fa_fwd.
+ */
+fa_status fa_fwd_varlen(const void *Q, const void *K, const void *V, void *O, float *LSE,
+                        const int *cu_seqlens, int nseq, int H, int total, int max_seqlen, int d,
+                        float scale, int causal, void *stream);
+
 /* Bytes of workspace fa_bwd needs: 2*B*H*S fp32 values (D and LSE*log2 e). */
 size_t fa_bwd_workspace_bytes(int B, int H, int S, int d);
 

@@ -113,3 +113,40 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         fa.forward(q, q, q)
+
+
+def fwd_varlen(lib, nseq=2, H=2, total=300, max_seqlen=200, d=128, scale=0.088, causal=0, ptrs=None, cu=A):
+    p = ptrs or [A, A, A, A, A]
+    return lib.fa_fwd_varlen(*p, cu, nseq, H, total, max_seqlen, d, ctypes.c_float(scale), causal, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(nseq=-1), 1), (dict(H=-1), 1), (dict(total=-3), 1), (dict(max_seqlen=-1), 1),
+    (dict(d=80), 2), (dict(scale=0.0), 1), (dict(scale=float("nan")), 1), (dict(causal=2), 1),
+    (dict(max_seqlen=(1 << 22) + 1), 1),
+    # total * H * d * 2 must stay below 2^32
+    (dict(total=1 << 20, H=16), 1),
+])
+def test_varlen_forward_rejects_bad_arguments(lib, kw, code):
+    assert fwd_varlen(lib, **kw) == code
+
+
+def test_varlen_forward_null_misaligned_and_empty(lib):
+    assert fwd_varlen(lib, cu=NULL) == 1
+    assert fwd_varlen(lib, cu=ctypes.c_void_p(0x10002)) == 1      # cu_seqlens not 4-byte aligned
+    assert fwd_varlen(lib, ptrs=[A, A, MIS, A, A]) == 1
+    assert fwd_varlen(lib, ptrs=[A, A, A, A, NULL]) == 1
+    # empty calls: nothing to compute, nothing dereferenced
+    assert fwd_varlen(lib, nseq=0, ptrs=[NULL] * 5, cu=NULL) == 0
+    assert fwd_varlen(lib, total=0, ptrs=[NULL] * 5, cu=NULL) == 0
+    assert fwd_varlen(lib, max_seqlen=0, ptrs=[NULL] * 5, cu=NULL) == 0
+    assert fwd_varlen(lib, H=0, ptrs=[NULL] * 5, cu=NULL) == 0
+
+
+def test_varlen_binding_checks_shapes():
+    torch = pytest.importorskip("torch")
+    import exact_attention_39_amd as fa
+    q = torch.zeros(10, 2, 64, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 4, 10], dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU"):
+        fa.forward_varlen(q, q, q, cu, 6)

@@ -287,3 +287,111 @@ def test_backward_is_bitwise_repeatable(fa):
         torch.cuda.synchronize()
         for a, b, nm in zip(g1, g2, ("dQ", "dK", "dV")):
             assert torch.equal(a, b), f"{nm} differs between runs (causal={causal})"
+
+
+# ------------------------------------------------------------------ packed variable-length forward
+VARLEN = [
+    # (sequence lengths, H, d, causal): empty, one-token, ragged and multi-tile sequences
+    ([0, 1, 37, 129, 256, 300, 515, 64], 3, 128, False),
+    ([0, 1, 37, 129, 256, 300, 515, 64], 3, 128, True),
+    ([200, 0, 131, 1], 2, 64, True),
+    ([1000, 17], 4, 128, True),
+]
+
+
+def varlen_case(lens, H, d, seed):
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    total = int(cu[-1])
+    qb, kb, vb = (rand_bits((total, H, d), seed + i) for i in range(3))
+    return cu, total, qb, kb, vb
+
+
+def seq_f64(bits, a, b):
+    """Tokens a..b-1 of a [total, H, d] bf16 tensor as an oracle [1, H, L, d] array."""
+    return np.ascontiguousarray(gen.bf16_bits_to_f64(bits[a:b]).transpose(1, 0, 2)[None])
+
+
+@pytest.mark.parametrize("lens,H,d,causal", VARLEN)
+def test_varlen_forward_matches_oracle_per_sequence(fa, lens, H, d, causal):
+    say(f"[varlen] lens={lens} H={H} d={d} causal={causal}")
+    cu, total, qb, kb, vb = varlen_case(lens, H, d, 7000 + d + int(causal) + len(lens))
+    scale = 1.0 / np.sqrt(d)
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    cu_d = torch.from_numpy(cu).cuda()
+    o, lse = fa.forward_varlen(q, k, v, cu_d, max(lens), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    o_np, lse_np = bf16_to_np64(o), lse.cpu().numpy().astype(np.float64)
+    for s in range(len(lens)):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if a == b:
+            continue
+        o_ref, lse_ref = oracle.attention_forward(seq_f64(qb, a, b), seq_f64(kb, a, b), seq_f64(vb, a, b),
+                                                  scale, causal)
+        check_o(o_np[a:b].transpose(1, 0, 2), o_ref[0], f"varlen seq {s} (len {b - a})")
+        check_lse(lse_np[:, a:b], lse_ref[0], f"varlen seq {s} (len {b - a})")
+
+
+def test_varlen_equals_dense_forward_bitwise(fa):
+    """Each sequence of a packed batch gives bit for bit what the dense
+    [1, H, L, d] forward gives: the same kernel, only the addressing differs."""
+    lens, H, d = [300, 1, 129, 640], 2, 128
+    say(f"[varlen vs dense] lens={lens}")
+    cu, total, qb, kb, vb = varlen_case(lens, H, d, 7100)
+    scale = 1.0 / np.sqrt(d)
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    cu_d = torch.from_numpy(cu).cuda()
+    for causal in (False, True):
+        o, lse = fa.forward_varlen(q, k, v, cu_d, max(lens), causal=causal, scale=scale)
+        for s in range(len(lens)):
+            a, b = int(cu[s]), int(cu[s + 1])
+            qs, ks, vs = (t[a:b].transpose(0, 1).unsqueeze(0).contiguous() for t in (q, k, v))
+            od, lsed = fa.forward(qs, ks, vs, causal=causal, scale=scale)
+            torch.cuda.synchronize()
+            assert torch.equal(o[a:b], od[0].transpose(0, 1)), f"O of sequence {s} (causal={causal})"
+            assert torch.equal(lse[:, a:b], lsed[0]), f"LSE of sequence {s} (causal={causal})"
+
+
+def test_varlen_clamps_offsets(fa):
+    """Offsets below 0 or past total are clamped (to 0 and total): the batch
+    then splits as [0, 30), [30, 30), [30, total)."""
+    H, d, total = 2, 128, 100
+    say("[varlen clamp] cu = [-5, 30, 30, 250], total 100")
+    qb, kb, vb = (rand_bits((total, H, d), 7200 + i) for i in range(3))
+    cu_d = torch.tensor([-5, 30, 30, 250], dtype=torch.int32).cuda()
+    scale = 1.0 / np.sqrt(d)
+    o, lse = fa.forward_varlen(to_dev(qb), to_dev(kb), to_dev(vb), cu_d, 128, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    o_np, lse_np = bf16_to_np64(o), lse.cpu().numpy().astype(np.float64)
+    for a, b in ((0, 30), (30, 100)):
+        o_ref, lse_ref = oracle.attention_forward(seq_f64(qb, a, b), seq_f64(kb, a, b), seq_f64(vb, a, b),
+                                                  scale, True)
+        check_o(o_np[a:b].transpose(1, 0, 2), o_ref[0], f"clamped [{a}, {b})")
+        check_lse(lse_np[:, a:b], lse_ref[0], f"clamped [{a}, {b})")
+
+
+def test_varlen_prefill_workload_sampled(fa):
+    """The packed prefill batch that bench.py --varlen times, in the same
+    launch configuration: sampled rows of the shortest, the longest and a
+    middle sequence, first and last head, against the oracle."""
+    name = "prefill_varlen_h16_d128"
+    w = gen.VARLEN_WORKLOADS[name]
+    say(f"[varlen workload] {name}")
+    lens, bits = gen.varlen_inputs(name)
+    _WORKLOAD_CACHE.clear()
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    H, d = w["H"], w["d"]
+    scale = gen.default_scale(d)
+    q, k, v = (to_dev(bits[t]) for t in ("q", "k", "v"))
+    o, lse = fa.forward_varlen(q, k, v, torch.from_numpy(cu).cuda(), int(lens.max()), causal=w["causal"],
+                               scale=scale)
+    torch.cuda.synchronize()
+    order = np.argsort(lens)
+    for s in (int(order[0]), int(order[len(order) // 2]), int(order[-1])):
+        a, b = int(cu[s]), int(cu[s + 1])
+        rows = sample_rows(b - a)
+        for h in (0, H - 1):
+            Q, K, V = (gen.bf16_bits_to_f64(bits[t][a:b, h]) for t in ("q", "k", "v"))
+            o_ref, l_ref = oracle.forward_rows(Q, K, V, rows, scale, w["causal"])
+            idx = torch.from_numpy(rows + a).cuda()
+            check_o(bf16_to_np64(o[idx, h]), o_ref, f"{name} seq {s} head {h}")
+            check_lse(lse[h, idx].cpu().numpy().astype(np.float64), l_ref, f"{name} seq {s} head {h}")

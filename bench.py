@@ -103,8 +103,21 @@ def _time(fn, reps=5):
     return e0.elapsed_time(e1) / reps
 
 
+def _sweep(configs, rounds=3):
+    """Median launch time of each (key, set_options, launch) in configs, the
+    configurations interleaved over `rounds` rounds so that clock and
+    warm-up drift do not favour any of them."""
+    times = {}
+    for _ in range(rounds):
+        for key, setup, fn in configs:
+            setup()
+            times.setdefault(key, []).append(_time(fn))
+    return {k: sorted(v)[len(v) // 2] for k, v in times.items()}
+
+
 def ablation(fa, gen, dev, q, k, v, do, B, H, S, d, scale):
-    """One JSON line: kernel times under each softmax option and causal order."""
+    """One JSON line: kernel times under each softmax option and causal order
+    (medians of three interleaved rounds)."""
     import torch
     o = torch.empty_like(q)
     lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
@@ -112,44 +125,49 @@ def ablation(fa, gen, dev, q, k, v, do, B, H, S, d, scale):
     dk, dv = torch.empty_like(q), torch.empty_like(q)
     ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, S, d) // 4, dtype=torch.float32, device="cuda")
     rows = []
-    for tau, poly, deg in [(8.0, 0, 3), (0.0, 0, 3), (8.0, 1, 3), (8.0, 2, 3), (8.0, 1, 5), (8.0, 2, 5)]:
-        fa.fa_set_softmax_options(tau, poly, deg)
-        for causal in (False, True):
-            ms = _time(lambda: fa.fa_fwd(q, k, v, o, lse, scale, causal))
-            fl = flops(B, H, S, d, causal, False)
-            rows.append({"kernel": "fwd", "workload": WORKLOAD, "causal": causal, "tau": tau,
-                         "poly_eighths": poly, "poly_degree": deg, "ms": round(ms, 4),
+    opts = [(8.0, 0, 3), (0.0, 0, 3), (8.0, 1, 3), (8.0, 2, 3), (8.0, 1, 5), (8.0, 2, 5)]
+
+    def option_rows(wname, qq, kk, vv, oo, ll, sc, shape, options, causals):
+        cfgs = [((opt, causal), (lambda opt=opt: fa.fa_set_softmax_options(*opt)),
+                 (lambda causal=causal: fa.fa_fwd(qq, kk, vv, oo, ll, sc, causal)))
+                for opt in options for causal in causals]
+        med = _sweep(cfgs)
+        for (opt, causal), ms in med.items():
+            fl = flops(*shape, causal, False)
+            rows.append({"kernel": "fwd", "workload": wname, "causal": causal, "tau": opt[0],
+                         "poly_eighths": opt[1], "poly_degree": opt[2], "ms": round(ms, 4),
                          "tflops": round(fl / ms / 1e9, 1)})
-    fa.fa_set_softmax_options(8.0, 0, 3)
-    # rescale threshold on the workload built to move the running max
-    wname = "causal_boost_b2_h16_s8192"
-    w = gen.WORKLOADS[wname]
-    bb = gen.workload_inputs(wname, ("q", "k", "v"))
-    qb, kb, vb = (dev(bb[t]) for t in "qkv")
-    ob = torch.empty_like(qb)
-    lb = torch.empty(qb.shape[:3], dtype=torch.float32, device="cuda")
-    sb = gen.default_scale(w["d"])
-    for tau in (0.0, 2.0, 8.0):
-        fa.fa_set_softmax_options(tau, 0, 3)
-        ms = _time(lambda: fa.fa_fwd(qb, kb, vb, ob, lb, sb, True))
-        fl = flops(w["B"], w["H"], w["S"], w["d"], True, False)
-        rows.append({"kernel": "fwd", "workload": wname, "causal": True, "tau": tau, "poly_eighths": 0,
-                     "poly_degree": 3, "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1)})
-    fa.fa_set_softmax_options(8.0, 0, 3)
+        fa.fa_set_softmax_options(8.0, 0, 3)
+
+    option_rows(WORKLOAD, q, k, v, o, lse, scale, (B, H, S, d), opts, (False, True))
+    # the same options at a shorter sequence (B = 4, H = 16, S = 4096), and
+    # the rescale threshold on the workload built to move the running max
+    for wname, options, causals in (("fwd_b4_h16_s4096", opts[:4], (False, True)),
+                                    ("causal_boost_b2_h16_s8192", [(0.0, 0, 3), (2.0, 0, 3), (8.0, 0, 3)],
+                                     (True,))):
+        w = gen.WORKLOADS[wname]
+        bb = gen.workload_inputs(wname, ("q", "k", "v"))
+        qs, ks, vs = (dev(bb[t]) for t in "qkv")
+        os_ = torch.empty_like(qs)
+        ls = torch.empty(qs.shape[:3], dtype=torch.float32, device="cuda")
+        option_rows(wname, qs, ks, vs, os_, ls, gen.default_scale(w["d"]), (w["B"], w["H"], w["S"], w["d"]),
+                    options, causals)
+        del qs, ks, vs, os_, ls
     # causal block order: longest first (LPT) vs shortest first
     fa.fa_fwd(q, k, v, o, lse, scale, True)
     fa.fa_bwd_preprocess(o, do, lse, ws)
-    for lpt in (True, False):
-        fa.fa_set_causal_order(lpt)
-        for name, fn, fl in (
-                ("fwd", lambda: fa.fa_fwd(q, k, v, o, lse, scale, True), flops(B, H, S, d, True, False)),
-                ("bwd_dkdv", lambda: fa.fa_bwd_dkdv(q, k, v, do, dk, dv, scale, True, ws),
-                 0.8 * flops(B, H, S, d, True, True)),
-                ("bwd_dq", lambda: fa.fa_bwd_dq(q, k, v, do, dq, scale, True, ws),
-                 0.2 * flops(B, H, S, d, True, True))):
-            ms = _time(fn)
-            rows.append({"kernel": name, "workload": WORKLOAD, "causal": True, "longest_first": lpt,
-                         "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1)})
+    kernels = (("fwd", lambda: fa.fa_fwd(q, k, v, o, lse, scale, True), flops(B, H, S, d, True, False)),
+               ("bwd_dkdv", lambda: fa.fa_bwd_dkdv(q, k, v, do, dk, dv, scale, True, ws),
+                0.8 * flops(B, H, S, d, True, True)),
+               ("bwd_dq", lambda: fa.fa_bwd_dq(q, k, v, do, dq, scale, True, ws),
+                0.2 * flops(B, H, S, d, True, True)))
+    cfgs = [((name, lpt), (lambda lpt=lpt: fa.fa_set_causal_order(lpt)), fn)
+            for lpt in (True, False) for name, fn, _ in kernels]
+    med = _sweep(cfgs)
+    fl_of = {name: fl for name, _, fl in kernels}
+    for (name, lpt), ms in med.items():
+        rows.append({"kernel": name, "workload": WORKLOAD, "causal": True, "longest_first": lpt,
+                     "ms": round(ms, 4), "tflops": round(fl_of[name] / ms / 1e9, 1)})
     fa.fa_set_causal_order(True)
     print(json.dumps({"ablation": rows}), flush=True)
 

@@ -6,19 +6,25 @@
 // attention, hyper.ai story; tiled pipeline, gist.science technical
 // summary, methodology item 1).
 //
-// Work decomposition
-//   * one workgroup = 4 waves = 128 query rows (32 per wave) of one head;
-//     two workgroups share a CU (256 VGPRs per wave, 64 KB LDS each), so
-//     each SIMD interleaves the MFMA phase of one wave with the softmax of
-//     the other -- the MFMA/softmax overlap the pages call ping-pong,
-//     obtained here from the SIMD's wave arbitration;
-//   * key/value tiles of 64 rows stream through LDS, double buffered: the
-//     direct memory-to-LDS copies of tile j+1 (buffer_load ... lds) are
-//     issued before tile j is computed and land in the other buffer;
-//   * per wave and tile: S^T = K Q^T (16 MFMA 32x32x16), online softmax in
-//     registers, O^T += V^T P^T (16 MFMA).  Keeping the transposed products
-//     puts the query index on the lanes, so row max, row sum and the
-//     rescale factor are per lane; only one v_permlane32_swap per tile
+// Work decomposition (warp specialisation, the MFMA/softmax overlap of the
+// gist.science technical summary, methodology item 1, mapped to CDNA4):
+//   * one workgroup = 8 waves = 256 query rows of one head, one workgroup
+//     per CU.  Waves 0-3 are score waves, waves 4-7 PV waves; wave w and
+//     wave w + 4 (one of each per SIMD) form a pair that owns 64 query rows
+//     as two halves of 32;
+//   * the score wave forms S^T = K Q^T for its 64 rows (16 MFMA 32x32x16
+//     per half; every K operand read from LDS feeds the MFMAs of both
+//     halves), runs the online softmax and hands P, already packed as the
+//     PV MFMA operand, plus the per-row rescale factors to its partner
+//     through LDS;
+//   * the PV wave holds O^T of the 64 rows and adds V^T P^T one tile later
+//     (every V^T operand feeds both halves).  On each SIMD the PV wave's
+//     MFMAs run while the score wave computes exponentials;
+//   * key/value tiles of 64 rows stream through LDS, K and V double
+//     buffered and filled by direct memory-to-LDS copies (buffer_load ...
+//     lds) one iteration ahead; one workgroup barrier per tile;
+//   * the transposed products put the query index on the lanes, so row max,
+//     row sum and the rescale factor are per lane; one v_permlane32_swap
 //     joins the two half-waves that hold the two halves of a row.
 //
 // Softmax (the pages' ideas, adapted):
@@ -44,8 +50,8 @@ namespace fa {
 
 namespace {
 
-constexpr int kFwdThreads = 256;
-constexpr int kBr = 128;  // query rows per workgroup
+constexpr int kFwdThreads = 512;  // waves 0-3 score waves, 4-7 PV waves (one of each per SIMD)
+constexpr int kBr = 256;  // query rows per workgroup: 64 per wave pair
 constexpr int kBc = 64;   // key/value rows per tile
 
 template <int POLY, int DEG>
@@ -63,7 +69,7 @@ __device__ __forceinline__ float exp2_sel(float x, int r) {
 // non-decreasing, so no access leaves the tensors whatever they hold.
 // Otherwise unit u is head u of a [BH][S][D] tensor, LSE [BH][S].
 template <int D, bool CAUSAL, int POLY, int DEG, bool VARLEN>
-__global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(
+__global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     uint16_t *__restrict__ O, float *__restrict__ LSE, int BH, int S_arg, float c, float tau, int nqb,
     int lpt, const int *__restrict__ cu, int H, int total) {
@@ -73,8 +79,16 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(
     constexpr int DB = D / 32;         // 32-wide d blocks of O^T
     constexpr int TILE = kBc * ROWB;   // bytes of one K or V tile
 
-    __shared__ __attribute__((aligned(1024))) char smem_raw[2 * 2 * TILE];
+    // LDS: K slots [2], V slots [2] (tile t in slot t & 1); P hand-off
+    // buffers [2] (P of tile t in buffer t & 1), per wave pair, query half
+    // sb and k-step u one 16-byte operand per lane; rescale factors [2]
+    // (the same indexing, one float per lane).
+    constexpr int PBUF = 4 * 2 * 4 * 64 * 16;
+    constexpr int ABUF = 4 * 2 * 64 * 4;
+    __shared__ __attribute__((aligned(1024))) char smem_raw[4 * TILE + 2 * PBUF + 2 * ABUF];
     fa_lds_char *smem = (fa_lds_char *)smem_raw;
+    fa_lds_char *sPb = smem + 4 * TILE;
+    fa_lds_char *sAb = sPb + 2 * PBUF;
 
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int h = lane >> 5, n = lane & 31;
@@ -105,8 +119,9 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(
     const int kv_end = CAUSAL ? min(S, q0 + kBr) : S;
     const int nkv = (kv_end + kBc - 1) / kBc;
 
-    const int qrow = q0 + 32 * w + n;   // this lane's query row
-    const int wq_lo = q0 + 32 * w;      // first query row of the wave
+    const int pair = w & 3;             // the 64 query rows q0 + 64 pair ..
+    const bool score_wave = w < 4;      // S^T and softmax; the partner does O^T += V^T P^T
+    const int prow0 = q0 + 64 * pair;   // first query row of the pair
 
     // Per-unit buffer resources end with row S - 1: rows at or past S read
     // as zero and are never written.
@@ -115,159 +130,219 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(
     const fa_rsrc rK = make_rsrc(K + head, head_bytes);
     const fa_rsrc rV = make_rsrc(V + head, head_bytes);
 
-    // Q^T as the B operand of S^T = K Q^T: lane holds Q[qrow][16ks + 8h .. +7].
-    fa_u32x4 qf[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = buf_load16(rQ, (uint32_t)qrow * pitch + (16 * ks + 8 * h) * 2);
-
-    fa_f32x16 oacc[DB];
-#pragma unroll
-    for (int i = 0; i < DB; ++i) oacc[i] = zero16();
-    float m_ref = -1.0e30f;  // finite sentinel: no inf - inf when a row's tile is fully masked
-    float l_sum = 0.0f;
-
-    auto issue_tile = [&](int j, int buf) {
-        fa_lds_char *sK = smem + buf * 2 * TILE;
-        tile_to_lds_pitched<NCH, kBc>(rK, j * kBc, pitch, sK, w, lane);
-        tile_to_lds_pitched<NCH, kBc>(rV, j * kBc, pitch, sK + TILE, w, lane);
+    auto issue_k = [&](int t) __attribute__((always_inline)) {
+        tile_to_lds_pitched<NCH, kBc, 8>(rK, t * kBc, pitch, smem + (t & 1) * TILE, w, lane);
+    };
+    auto issue_v = [&](int t) __attribute__((always_inline)) {
+        tile_to_lds_pitched<NCH, kBc, 8>(rV, t * kBc, pitch, smem + (2 + (t & 1)) * TILE, w, lane);
+    };
+    // this lane's 16-byte P operand of half sb, k-step u in buffer b, and
+    // its rescale factor of half sb
+    auto p_slot = [&](int b, int sb, int u) __attribute__((always_inline)) {
+        return sPb + b * PBUF + (((pair * 2 + sb) * 4 + u) * 64 + lane) * 16;
+    };
+    auto a_slot = [&](int b, int sb) __attribute__((always_inline)) {
+        return sAb + b * ABUF + ((pair * 2 + sb) * 64 + lane) * 4;
     };
 
-    // Lane-dependent LDS offsets, computed once.  Row reads of key row
-    // 32 mb + n at chunk 2 ks + h: the swizzle only sees the low 4 bits of
-    // the row, so mb is an immediate (32 rows) and one offset per ks remains.
-    // Transposing reads of V rows 16 t + 4 h + 8 s + L/4: the swizzle is the
-    // same for every t, so t is an immediate and one offset per (db, s)
-    // remains.
-    int koff[KS], voff[DB][2];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) koff[ks] = tile_off<NCH>(n, (2 * ks + h) * 16);
-    {
-        const int L = lane & 15;
-        const int col = ((lane >> 4) & 1) * 16 + (L & 3) * 4;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) voff[db][s2] = tile_off<NCH>(4 * h + 8 * s2 + (L >> 2), (32 * db + col) * 2);
-    }
-
-    // One key/value tile from LDS buffer BUF (a compile-time constant, so
-    // every LDS address is a loop-invariant register plus an immediate).
-    // MASK: the tile crosses this wave's diagonal or the end of the sequence.
-    auto compute_tile = [&](int buf, auto MASKC, int kv0) {
-        constexpr bool MASK = decltype(MASKC)::value;
-        const fa_lds_char *sK = smem + buf * 2 * TILE;
-        const fa_lds_char *sV = sK + TILE;
-        // S^T = K Q^T for 64 keys x 32 queries: two 32x32 blocks.
-        fa_f32x16 sacc[2] = {zero16(), zero16()};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                const fa_u32x4 a = lds_read16(sK + 32 * mb * ROWB, koff[ks]);
-                sacc[mb] = mfma32(a, qf[ks], sacc[mb]);
-            }
-        }
-        if constexpr (MASK) {
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int kv = kv0 + 32 * mb + 8 * (r >> 2) + 4 * h + (r & 3);
-                    const bool dead = (CAUSAL && kv > qrow) || kv >= S;
-                    sacc[mb][r] = dead ? -INFINITY : sacc[mb][r];
-                }
-        }
-        // row max over this lane's 32 keys, then across the two half-waves
-        float mx = sacc[0][0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][r]);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][r]);
-        mx = max_halves(mx);
-        const float m_new = mx * c;
-        const bool need = m_new > m_ref + tau;
-        if (__builtin_amdgcn_ballot_w64(need)) {
-            const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
-            m_ref = need ? m_new : m_ref;
-            l_sum *= alpha;
-#pragma unroll
-            for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
-        }
-        const float nm = -m_ref;
-        // P = 2^(s c - m_ref), packed to bf16 in MFMA k order.  The row sum
-        // adds the fp32 values (two partial sums): summing the bf16-rounded
-        // ones would put up to 2^-9 relative error into the LSE of rows with
-        // few keys.
-        fa_u32x4 pf[4];
-        float la = 0.0f, lb = 0.0f;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const float p0 = exp2_sel<POLY, DEG>(fmaf(sacc[mb][r], c, nm), r);
-                const float p1 = exp2_sel<POLY, DEG>(fmaf(sacc[mb][r + 1], c, nm), r + 1);
-                la += p0;
-                lb += p1;
-                pf[2 * mb + (r >> 3)][(r & 7) >> 1] = pack_bf16(p0, p1);
-            }
-        }
-        l_sum += la + lb;
-        // O^T += V^T P^T, k-step t covers keys 16t .. 16t+15 of the tile in
-        // accumulator order; V^T operand by transposing reads of V rows.
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const fa_u32x2 lo = lds_read_tr(sV + 16 * t * ROWB, voff[db][0]);
-                const fa_u32x2 hi = lds_read_tr(sV + 16 * t * ROWB, voff[db][1]);
-                const fa_u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-                oacc[db] = mfma32(a, pf[t], oacc[db]);
-            }
-        }
-    };
-
-    // One loop step: prefetch tile j+1 into the other buffer, compute tile j,
-    // then wait for the prefetch and synchronise.  Interior tiles (no key
-    // past the diagonal of any row of the workgroup, none past S) run
-    // without masking in a first loop; the at most two boundary tiles run
-    // masked in a second loop, where a wave whose rows all lie above the
-    // tile skips the compute.
-    auto step = [&](int j, auto MASKC) {
-        const int buf = j & 1;
-        if (j + 1 < nkv) issue_tile(j + 1, buf ^ 1);
-        const int kv0 = j * kBc;
-        if constexpr (decltype(MASKC)::value) {
-            if (!(CAUSAL && kv0 > wq_lo + 31)) compute_tile(buf, MASKC, kv0);
-        } else {
-            compute_tile(buf, MASKC, kv0);
-        }
-        wait_vmem();      // tile j+1 has landed in the other buffer
-        __syncthreads();  // ... for every wave, and nobody still reads this one
-    };
-
-    if (nkv > 0) issue_tile(0, 0);
+    // Iteration j (0 <= j <= nkv): the copies of K_{j+1} and V_j start; the
+    // score wave turns tile j into P(j); the PV wave adds tile j - 1 to O.
+    // K_{j+1} and V_j go to the slots last read in iteration j - 1 (K_{j-1}
+    // by the score wave, V_{j-2} by the PV wave); P(j) to the buffer the PV
+    // wave read in iteration j - 1.  One barrier per iteration.
+    const int n_plain = min(nkv, (CAUSAL ? min(q0, S) : S) / kBc);
+    issue_k(0);
     wait_vmem();
     __syncthreads();
 
-    const int n_plain = min(nkv, (CAUSAL ? min(q0, S) : S) / kBc);
-    for (int j = 0; j < n_plain; ++j) step(j, std::false_type{});
-    for (int j = n_plain; j < nkv; ++j) step(j, std::true_type{});
+    if (score_wave) {
+        // ------------------------------------------------ score wave
+        // Q^T of both halves as B operands: lane holds Q[row][16ks + 8h .. +7].
+        fa_u32x4 qf[2][KS];
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                qf[sb][ks] = buf_load16(rQ, (uint32_t)(prow0 + 32 * sb + n) * pitch + (16 * ks + 8 * h) * 2);
+        float m_ref[2] = {-1.0e30f, -1.0e30f};  // finite sentinel: no inf - inf for fully masked rows
+        float l_sum[2] = {0.0f, 0.0f};
+        // Row reads of key row 32 mb + n at chunk 2 ks + h: the swizzle only
+        // sees the low 4 bits of the row, so mb is an immediate.
+        int koff[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) koff[ks] = tile_off<NCH>(n, (2 * ks + h) * 16);
 
-    // Epilogue: join the half-row sums, normalise, store O (bf16) and LSE.
-    const float l_tot = sum_halves(l_sum);
-    const float inv = 1.0f / l_tot;
-    const fa_rsrc rO = make_rsrc(O + head, head_bytes);
+        // S^T = K_t Q^T, 64 keys x 2 halves of 32 queries; each K operand
+        // feeds the MFMAs of both halves.
+        fa_f32x16 sacc[2][2];
+        auto s_product = [&](int t) __attribute__((always_inline)) {
+            const fa_lds_char *sK = smem + (t & 1) * TILE;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+            for (int sb = 0; sb < 2; ++sb) sacc[sb][0] = sacc[sb][1] = zero16();
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            fa_u32x2 v = {pack_bf16(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
-                          pack_bf16(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
-            buf_store8(rO, (uint32_t)qrow * pitch + (32 * db + 8 * g + 4 * h) * 2, v);
-        }
-    if (h == 0) {
+            for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb) {
+                    const fa_u32x4 a = lds_read16(sK + 32 * mb * ROWB, koff[ks]);
+#pragma unroll
+                    for (int sb = 0; sb < 2; ++sb) sacc[sb][mb] = mfma32(a, qf[sb][ks], sacc[sb][mb]);
+                }
+            }
+        };
+
+        // Online softmax of S^T(t) into P(t) and the rescale factors, both
+        // handed to the PV wave through buffer t & 1.
+        auto softmax = [&](int t, auto MASKC) __attribute__((always_inline)) {
+            const int kv0 = t * kBc;
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+                const int qrow = prow0 + 32 * sb + n;
+                if constexpr (decltype(MASKC)::value) {
+#pragma unroll
+                    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int kv = kv0 + 32 * mb + 8 * (r >> 2) + 4 * h + (r & 3);
+                            const bool dead = (CAUSAL && kv > qrow) || kv >= S;
+                            sacc[sb][mb][r] = dead ? -INFINITY : sacc[sb][mb][r];
+                        }
+                }
+                // row max over this lane's 32 keys, then across the half-waves
+                float mx = sacc[sb][0][0];
+#pragma unroll
+                for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[sb][0][r]);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][1][r]);
+                mx = max_halves(mx);
+                const float m_new = mx * c;
+                const bool need = m_new > m_ref[sb] + tau;
+                const float alpha = need ? __builtin_amdgcn_exp2f(m_ref[sb] - m_new) : 1.0f;
+                m_ref[sb] = need ? m_new : m_ref[sb];
+                const float nm = -m_ref[sb];
+                // P = 2^(s c - m_ref), packed to bf16 in MFMA k order.  The
+                // row sum adds the fp32 values (two partial sums): summing
+                // the bf16-rounded ones would put up to 2^-9 relative error
+                // into the LSE of rows with few keys.
+                float la = 0.0f, lb = 0.0f;
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+                    for (int r8 = 0; r8 < 16; r8 += 8) {
+                        fa_u32x4 pk;
+#pragma unroll
+                        for (int r = r8; r < r8 + 8; r += 2) {
+                            const float p0 = exp2_sel<POLY, DEG>(fmaf(sacc[sb][mb][r], c, nm), r);
+                            const float p1 = exp2_sel<POLY, DEG>(fmaf(sacc[sb][mb][r + 1], c, nm), r + 1);
+                            la += p0;
+                            lb += p1;
+                            pk[(r & 7) >> 1] = pack_bf16(p0, p1);
+                        }
+                        lds_write16(p_slot(t & 1, sb, 2 * mb + (r8 >> 3)), 0, pk);
+                    }
+                }
+                l_sum[sb] = fmaf(l_sum[sb], alpha, la + lb);
+                *(__attribute__((address_space(3))) float *)a_slot(t & 1, sb) = alpha;
+            }
+        };
+
+        // Iteration j: S^T(j), then its softmax.
+        auto iteration = [&](int j, auto MASKC) __attribute__((always_inline)) {
+            if (j + 1 < nkv) issue_k(j + 1);
+            if (j < nkv) issue_v(j);
+            if (j < nkv) {
+                s_product(j);
+                softmax(j, MASKC);
+            }
+            wait_vmem();
+            __syncthreads();
+        };
+        int j = 0;
+        for (; j < n_plain; ++j) iteration(j, std::false_type{});
+        for (; j <= nkv; ++j) iteration(j, std::true_type{});
+
+        // hand the row sums and reference maxima to the PV wave; store LSE
         const fa_rsrc rL = make_rsrc(LSE + lse0, (uint32_t)S * 4);
-        buf_store4(rL, (uint32_t)qrow * 4, __float_as_uint((m_ref + __log2f(l_tot)) * FA_LN2));
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            const float l_tot = sum_halves(l_sum[sb]);
+            *(__attribute__((address_space(3))) float *)a_slot(0, sb) = l_tot;
+            if (h == 0)
+                buf_store4(rL, (uint32_t)(prow0 + 32 * sb + n) * 4,
+                           __float_as_uint((m_ref[sb] + __log2f(l_tot)) * FA_LN2));
+        }
+        __syncthreads();
+    } else {
+        // ------------------------------------------------ PV wave
+        fa_f32x16 oacc[2][DB];
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) oacc[sb][db] = zero16();
+        // Transposing reads of V rows 16 u + 4 h + 8 s + L/4: the swizzle is
+        // the same for every u, so u is an immediate and one offset per
+        // (db, s) remains.
+        int voff[DB][2];
+        {
+            const int L = lane & 15;
+            const int col = ((lane >> 4) & 1) * 16 + (L & 3) * 4;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+                    voff[db][s2] = tile_off<NCH>(4 * h + 8 * s2 + (L >> 2), (32 * db + col) * 2);
+        }
+
+        // O^T = alpha O^T + V^T P^T for tile t (P(t) in buffer t & 1, V_t in
+        // V slot t & 1); each V^T operand feeds the MFMAs of both halves.
+        auto pv_tile = [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+                const float alpha = *(const __attribute__((address_space(3))) float *)a_slot(t & 1, sb);
+                if (__builtin_amdgcn_ballot_w64(alpha < 1.0f)) {
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) oacc[sb][db] *= alpha;
+                }
+            }
+            const fa_lds_char *sV = smem + (2 + (t & 1)) * TILE;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const fa_u32x4 p0 = lds_read16(p_slot(t & 1, 0, u), 0);
+                const fa_u32x4 p1 = lds_read16(p_slot(t & 1, 1, u), 0);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const fa_u32x2 lo = lds_read_tr(sV + 16 * u * ROWB, voff[db][0]);
+                    const fa_u32x2 hi = lds_read_tr(sV + 16 * u * ROWB, voff[db][1]);
+                    const fa_u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+                    oacc[0][db] = mfma32(a, p0, oacc[0][db]);
+                    oacc[1][db] = mfma32(a, p1, oacc[1][db]);
+                }
+            }
+        };
+
+        for (int j = 0; j <= nkv; ++j) {
+            if (j + 1 < nkv) issue_k(j + 1);
+            if (j < nkv) issue_v(j);
+            if (j >= 1) pv_tile(j - 1);
+            wait_vmem();
+            __syncthreads();
+        }
+        __syncthreads();  // the score wave's row sums are in the buffer
+
+        // Epilogue: normalise, store O (bf16).
+        const fa_rsrc rO = make_rsrc(O + head, head_bytes);
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            const float inv = 1.0f / *(const __attribute__((address_space(3))) float *)a_slot(0, sb);
+            const int qrow = prow0 + 32 * sb + n;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    fa_u32x2 v = {pack_bf16(oacc[sb][db][4 * g] * inv, oacc[sb][db][4 * g + 1] * inv),
+                                  pack_bf16(oacc[sb][db][4 * g + 2] * inv, oacc[sb][db][4 * g + 3] * inv)};
+                    buf_store8(rO, (uint32_t)qrow * pitch + (32 * db + 8 * g + 4 * h) * 2, v);
+                }
+        }
     }
 }
 

@@ -34,7 +34,10 @@
 //     and P may reach 2^tau (gist.science German explainer, section 3: skip
 //     the rescale when the numbers do not grow too large).  The decision is
 //     per row, the multiply is skipped for the whole wave when no row needs
-//     it.  The result does not depend on tau beyond rounding;
+//     it.  The result does not depend on tau beyond rounding.  P is formed
+//     against the reference first; the row maxima are only taken when some
+//     lane's partial row sum exceeds 2^tau (then some P may have), which
+//     leaves the common tile with no max reduction at all;
 //   * hybrid exp2: POLY eighths of the exponentials (a static subset of the
 //     registers) use the FMA polynomial of exp2_poly.h, the rest v_exp_f32
 //     (technical summary, methodology item 2);
@@ -191,38 +194,30 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(
         };
 
         // Online softmax of S^T(t) into P(t) and the rescale factors, both
-        // handed to the PV wave through buffer t & 1.
+        // handed to the PV wave through buffer t & 1.  tau_pow sits just
+        // below 2^tau, so that a P of 2^tau times (1 - 1 ulp) from a row max
+        // exactly tau past its reference still takes the row-max path.
+        const float tau_pow = __builtin_amdgcn_exp2f(tau) * 0.999f;
         auto softmax = [&](int t, auto MASKC) __attribute__((always_inline)) {
             const int kv0 = t * kBc;
+            if constexpr (decltype(MASKC)::value) {
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-                const int qrow = prow0 + 32 * sb + n;
-                if constexpr (decltype(MASKC)::value) {
+                for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
                     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             const int kv = kv0 + 32 * mb + 8 * (r >> 2) + 4 * h + (r & 3);
-                            const bool dead = (CAUSAL && kv > qrow) || kv >= S;
+                            const bool dead = (CAUSAL && kv > prow0 + 32 * sb + n) || kv >= S;
                             sacc[sb][mb][r] = dead ? -INFINITY : sacc[sb][mb][r];
                         }
-                }
-                // row max over this lane's 32 keys, then across the half-waves
-                float mx = sacc[sb][0][0];
-#pragma unroll
-                for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[sb][0][r]);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][1][r]);
-                mx = max_halves(mx);
-                const float m_new = mx * c;
-                const bool need = m_new > m_ref[sb] + tau;
-                const float alpha = need ? __builtin_amdgcn_exp2f(m_ref[sb] - m_new) : 1.0f;
-                m_ref[sb] = need ? m_new : m_ref[sb];
-                const float nm = -m_ref[sb];
-                // P = 2^(s c - m_ref), packed to bf16 in MFMA k order.  The
-                // row sum adds the fp32 values (two partial sums): summing
-                // the bf16-rounded ones would put up to 2^-9 relative error
-                // into the LSE of rows with few keys.
+            }
+            // P = 2^(s c - m_ref) of half sb, packed to bf16 in MFMA k order
+            // and handed over; returns the lane's partial row sum.  The row
+            // sum adds the fp32 values (two partial sums): summing the
+            // bf16-rounded ones would put up to 2^-9 relative error into the
+            // LSE of rows with few keys.
+            auto form_p = [&](int sb, float nm) __attribute__((always_inline)) {
                 float la = 0.0f, lb = 0.0f;
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb) {
@@ -240,8 +235,42 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(
                         lds_write16(p_slot(t & 1, sb, 2 * mb + (r8 >> 3)), 0, pk);
                     }
                 }
-                l_sum[sb] = fmaf(l_sum[sb], alpha, la + lb);
-                *(__attribute__((address_space(3))) float *)a_slot(t & 1, sb) = alpha;
+                return la + lb;
+            };
+            // P is first formed against the current reference max.  If no
+            // lane's partial row sum exceeds 2^tau, no P exceeds 2^tau, so no
+            // row max has moved more than tau past its reference: that is the
+            // result, and no row max is taken.  Otherwise (a larger or
+            // non-finite sum; always on a row's first tile, whose reference
+            // is the finite sentinel) take the row maxima, move the reference
+            // of the rows whose max exceeds it by more than tau, and form P
+            // again for a half in which any row moved.
+            float part[2], alpha[2] = {1.0f, 1.0f};
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) part[sb] = form_p(sb, -m_ref[sb]);
+            if (__builtin_amdgcn_ballot_w64(!(part[0] <= tau_pow) || !(part[1] <= tau_pow))) {
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb) {
+                    // row max over this lane's 32 keys, then across the half-waves
+                    float mx = sacc[sb][0][0];
+#pragma unroll
+                    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[sb][0][r]);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][1][r]);
+                    mx = max_halves(mx);
+                    const float m_new = mx * c;
+                    const bool need = m_new > m_ref[sb] + tau;
+                    if (__builtin_amdgcn_ballot_w64(need)) {
+                        alpha[sb] = need ? __builtin_amdgcn_exp2f(m_ref[sb] - m_new) : 1.0f;
+                        m_ref[sb] = need ? m_new : m_ref[sb];
+                        part[sb] = form_p(sb, -m_ref[sb]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+                l_sum[sb] = fmaf(l_sum[sb], alpha[sb], part[sb]);
+                *(__attribute__((address_space(3))) float *)a_slot(t & 1, sb) = alpha[sb];
             }
         };
 

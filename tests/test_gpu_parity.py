@@ -170,6 +170,50 @@ def test_forward_repeatable_and_rescale_options_agree(fa):
         fa.fa_set_softmax_options(8.0, 0, 3)
 
 
+def test_reference_max_paths(fa):
+    """The forward forms P against the running reference max first and takes
+    row maxima only when a partial row sum exceeds 2^tau.  Equal scores (Q =
+    0: every P is 1, so with tau = 2 every tile takes the row-max path and no
+    row moves) must give the closed form, mean of V over the allowed keys and
+    LSE = log(count); keys whose scores jump by more than tau in the last tile
+    must move the reference there."""
+    say("[ab] reference-max paths")
+    B, H, S, d = 1, 2, 700, 128
+    shape = (B, H, S, d)
+    scale = 1.0 / np.sqrt(d)
+    kb, vb = rand_bits(shape, 91), rand_bits(shape, 92)
+    V = gen.bf16_bits_to_f64(vb)
+    zero = np.zeros(shape, dtype=np.uint16)  # bf16 +0.0
+    try:
+        for tau in (8.0, 2.0, 0.0):
+            fa.fa_set_softmax_options(tau, 0, 3)
+            for causal in (False, True):
+                _, _, _, o, lse = run_fwd(fa, zero, kb, vb, causal, scale)
+                cnt = np.arange(1, S + 1, dtype=np.float64) if causal else np.full(S, float(S))
+                o_ref = (np.cumsum(V, axis=2) / cnt[:, None]) if causal else np.broadcast_to(V.mean(axis=2, keepdims=True), shape)
+                what = f"Q=0 tau={tau} causal={causal}"
+                check_o(bf16_to_np64(o), o_ref, what)
+                check_lse(lse.cpu().numpy().astype(np.float64), np.broadcast_to(np.log(cnt), (B, H, S)), what)
+        # late jump: keys S-50.. get +96 on every raw score (12 in log2 units)
+        q = gen.bf16_bits_to_f64(rand_bits(shape, 93)).astype(np.float32)
+        k = gen.bf16_bits_to_f64(kb).astype(np.float32)
+        q[..., 0] = 8.0
+        k[..., : S - 50, 0] = 0.0
+        k[..., S - 50:, 0] = 12.0
+        qb2, kb2 = gen.f32_to_bf16_bits(q), gen.f32_to_bf16_bits(k)
+        Q2, K2 = gen.bf16_bits_to_f64(qb2), gen.bf16_bits_to_f64(kb2)
+        for tau in (8.0, 2.0):
+            fa.fa_set_softmax_options(tau, 0, 3)
+            for causal in (False, True):
+                o_ref, l_ref = oracle.attention_forward(Q2, K2, V, scale, causal)
+                _, _, _, o, lse = run_fwd(fa, qb2, kb2, vb, causal, scale)
+                what = f"late jump tau={tau} causal={causal}"
+                check_o(bf16_to_np64(o), o_ref, what)
+                check_lse(lse.cpu().numpy().astype(np.float64), l_ref, what)
+    finally:
+        fa.fa_set_softmax_options(8.0, 0, 3)
+
+
 def test_device_exp2_polynomial(fa):
     say("[exp2] device polynomial")
     x = np.concatenate([np.linspace(-126.0, 0.0, 1 << 20), np.linspace(0.0, 8.0, 1 << 16),

@@ -65,12 +65,89 @@ __device__ __forceinline__ float exp2_sel(float x, int r) {
     return __builtin_amdgcn_exp2f(x);
 }
 
-// VARLEN: packed variable-length batch.  Workgroup (unit u, block qi) with
-// u = blockIdx % BH takes sequence u / H, head u % H; its rows are tokens
-// cu[s] .. cu[s+1]-1 of a [total][H][D] tensor (row pitch H * D elements),
-// LSE is [H][total].  cu entries are clamped to [0, total] and made
-// non-decreasing, so no access leaves the tensors whatever they hold.
-// Otherwise unit u is head u of a [BH][S][D] tensor, LSE [BH][S].
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    return __builtin_amdgcn_readfirstlane(v);
+}
+
+// Work item (sequence, query block) g of a packed batch, in longest-first
+// order, or !valid past the last item.  The cost of an item is its number of
+// key tiles: qblk + 1 blocks' worth when causal, the whole sequence when
+// not.  Items are grouped by cost level, highest first (causal: level =
+// qblk, one item per sequence with more blocks; non-causal: level = blocks
+// of the sequence - 1, all blocks of each such sequence), and by sequence
+// index within a level.  So no early-exit workgroups sit between the
+// working ones, whatever the order of the sequences in the batch.  Every
+// wave computes this on its own from cu (no LDS, no barrier); the level is
+// found by bisection over F(c) = number of items at levels >= c.  Blocks of a
+// sequence past nqb (a sequence longer than max_seqlen) are not counted.
+struct VarlenItem {
+    int seq, qblk;
+    bool valid;
+};
+
+template <bool CAUSAL>
+__device__ VarlenItem varlen_item(const int *__restrict__ cu, int nseq, int total, int nqb, int g, int lpt,
+                                  int lane) {
+    auto nb_at = [&](int s) -> int {
+        if (s >= nseq) return 0;
+        const int a = min(max(cu[s], 0), total);
+        const int b = min(max(cu[s + 1], a), total);
+        return min((b - a + kBr - 1) / kBr, nqb);
+    };
+    const int nb0 = nb_at(lane);  // the first 64 sequences, kept
+    auto nb_chunk = [&](int s0) { return s0 == 0 ? nb0 : nb_at(s0 + lane); };
+    auto F = [&](int c) -> int {
+        int acc = 0;
+        for (int s0 = 0; s0 < nseq; s0 += 64) {
+            const int nb = nb_chunk(s0);
+            acc += wave_sum(CAUSAL ? max(0, nb - c) : (nb > c ? nb : 0));
+        }
+        return acc;
+    };
+    VarlenItem it{0, 0, false};
+    const int items = F(0);
+    if (g >= items) return it;
+    if (!lpt) g = items - 1 - g;
+    int lo = 0, hi = nqb, f_hi = 0;  // F(lo) > g >= F(hi)
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        const int f = F(mid);
+        if (f > g) {
+            lo = mid;
+        } else {
+            hi = mid;
+            f_hi = f;
+        }
+    }
+    // item r of level lo: causal, the r-th sequence with more than lo
+    // blocks; otherwise block r % (lo + 1) of the r / (lo + 1)-th sequence
+    // with exactly lo + 1 blocks
+    const int r = g - f_hi;
+    int k = CAUSAL ? r : r / (lo + 1);
+    it.qblk = CAUSAL ? lo : r - k * (lo + 1);
+    for (int s0 = 0; s0 < nseq; s0 += 64) {
+        const int nb = nb_chunk(s0);
+        uint64_t m = __builtin_amdgcn_ballot_w64(CAUSAL ? nb > lo : nb == lo + 1);
+        const int cnt = __builtin_popcountll(m);
+        if (k < cnt) {
+            for (int i = 0; i < k; ++i) m &= m - 1;
+            it.seq = s0 + __builtin_ctzll(m);
+            it.valid = true;
+            return it;
+        }
+        k -= cnt;
+    }
+    return it;  // not reached: F counted the item
+}
+
+// VARLEN: packed variable-length batch; the workgroup's sequence, head and
+// query block come from varlen_item.  Its rows are tokens cu[s] .. cu[s+1]-1
+// of a [total][H][D] tensor (row pitch H * D elements), LSE is [H][total].
+// cu entries are clamped to [0, total] and made non-decreasing, so no access
+// leaves the tensors whatever they hold.  Otherwise unit u = blockIdx % BH
+// is head u of a [BH][S][D] tensor, LSE [BH][S].
 template <int D, bool CAUSAL, int POLY, int DEG, bool VARLEN>
 __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
@@ -96,29 +173,34 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int h = lane >> 5, n = lane & 31;
 
-    const int bh = blockIdx.x % BH;
-    const int qi = blockIdx.x / BH;
-    const int qblk = (CAUSAL && lpt) ? (nqb - 1 - qi) : qi;
-    const int q0 = qblk * kBr;
+    int qblk;             // query block of this workgroup
     int S;                // rows of this unit
     size_t head;          // element offset of its row 0
     size_t lse0;          // index of its row 0 in LSE
     uint32_t pitch;       // bytes between consecutive rows
     if constexpr (VARLEN) {
-        const int seq = bh / H, hh = bh - seq * H;
-        const int start = min(max(cu[seq], 0), total);
-        const int end = min(max(cu[seq + 1], start), total);
+        // Heads innermost: workgroup b takes head b % H of work item b / H
+        // (a sequence and one of its query blocks) in longest-first order.
+        const int hh = blockIdx.x % H;
+        const VarlenItem it = varlen_item<CAUSAL>(cu, BH / H, total, nqb, blockIdx.x / H, lpt, lane);
+        if (!it.valid) return;  // whole workgroup, before any barrier
+        qblk = it.qblk;
+        const int start = min(max(cu[it.seq], 0), total);
+        const int end = min(max(cu[it.seq + 1], start), total);
         S = end - start;
-        if (q0 >= S) return;  // whole workgroup, before any barrier
         head = ((size_t)start * H + hh) * D;
         lse0 = (size_t)hh * total + start;
         pitch = (uint32_t)H * ROWB;
     } else {
+        const int bh = blockIdx.x % BH;
+        const int qi = blockIdx.x / BH;
+        qblk = (CAUSAL && lpt) ? (nqb - 1 - qi) : qi;
         S = S_arg;
         head = (size_t)bh * (size_t)S * D;
         lse0 = (size_t)bh * S;
         pitch = ROWB;
     }
+    const int q0 = qblk * kBr;
     const int kv_end = CAUSAL ? min(S, q0 + kBr) : S;
     const int nkv = (kv_end + kBc - 1) / kBc;
 

@@ -413,6 +413,64 @@ def test_varlen_clamps_offsets(fa):
         check_lse(lse_np[:, a:b], lse_ref[0], f"clamped [{a}, {b})")
 
 
+def test_varlen_many_sequences_and_work_order(fa):
+    """More than 64 sequences (the work-item search walks the offsets in
+    chunks of 64), zero-length ones among them, in no particular order; the
+    longest-first and reversed work orders give the same bits."""
+    rng = np.random.default_rng(7300)
+    lens = [int(x) for x in rng.integers(0, 600, 150)]
+    lens[3] = lens[77] = 0
+    H, d = 2, 64
+    say(f"[varlen many] {len(lens)} sequences, {sum(lens)} tokens")
+    cu, total, qb, kb, vb = varlen_case(lens, H, d, 7300)
+    scale = 1.0 / np.sqrt(d)
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    cu_d = torch.from_numpy(cu).cuda()
+    try:
+        for causal in (False, True):
+            fa.fa_set_causal_order(True)
+            o, lse = fa.forward_varlen(q, k, v, cu_d, max(lens), causal=causal, scale=scale)
+            fa.fa_set_causal_order(False)
+            o2, lse2 = fa.forward_varlen(q, k, v, cu_d, max(lens), causal=causal, scale=scale)
+            torch.cuda.synchronize()
+            assert torch.equal(o, o2) and torch.equal(lse, lse2), f"work order changed the result (causal={causal})"
+            o_np, lse_np = bf16_to_np64(o), lse.cpu().numpy().astype(np.float64)
+            for si in range(len(lens)):
+                a, b = int(cu[si]), int(cu[si + 1])
+                if a == b:
+                    continue
+                o_ref, lse_ref = oracle.attention_forward(seq_f64(qb, a, b), seq_f64(kb, a, b), seq_f64(vb, a, b),
+                                                          scale, causal)
+                check_o(o_np[a:b].transpose(1, 0, 2), o_ref[0], f"seq {si} (len {b - a}, causal={causal})")
+                check_lse(lse_np[:, a:b], lse_ref[0], f"seq {si} (len {b - a}, causal={causal})")
+    finally:
+        fa.fa_set_causal_order(True)
+
+
+def test_varlen_rows_past_max_seqlen_untouched(fa):
+    """max_seqlen below a sequence's length: the launch covers
+    ceil(max_seqlen / 256) query blocks per sequence; rows past them keep
+    what the output held, rows before them are exact."""
+    lens, H, d, maxlen = [700, 100], 2, 128, 300   # 2 blocks: rows 0..511 of sequence 0
+    say(f"[varlen max_seqlen] lens={lens} max_seqlen={maxlen}")
+    cu, total, qb, kb, vb = varlen_case(lens, H, d, 7400)
+    scale = 1.0 / np.sqrt(d)
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    cu_d = torch.from_numpy(cu).cuda()
+    for causal in (False, True):
+        o = torch.full((total, H, d), 1024.0, device="cuda").to(torch.bfloat16)
+        lse = torch.full((H, total), -7.0, device="cuda")
+        fa.fa_fwd_varlen(q, k, v, o, lse, cu_d, maxlen, scale, causal)
+        torch.cuda.synchronize()
+        o_np, lse_np = bf16_to_np64(o), lse.cpu().numpy().astype(np.float64)
+        assert np.all(o_np[512:700] == 1024.0) and np.all(lse_np[:, 512:700] == -7.0), "rows past the blocks written"
+        for a, b, rows in ((0, 700, 512), (700, 800, 100)):
+            o_ref, lse_ref = oracle.attention_forward(seq_f64(qb, a, b), seq_f64(kb, a, b), seq_f64(vb, a, b),
+                                                      scale, causal)
+            check_o(o_np[a:a + rows].transpose(1, 0, 2), o_ref[0][:, :rows], f"[{a}, {b}) causal={causal}")
+            check_lse(lse_np[:, a:a + rows], lse_ref[0][:, :rows], f"[{a}, {b}) causal={causal}")
+
+
 def test_varlen_prefill_workload_sampled(fa):
     """The packed prefill batch that bench.py --varlen times, in the same
     launch configuration: sampled rows of the shortest, the longest and a

@@ -279,8 +279,11 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(
         // handed to the PV wave through buffer t & 1.  tau_pow sits just
         // below 2^tau, so that a P of 2^tau times (1 - 1 ulp) from a row max
         // exactly tau past its reference still takes the row-max path.
+        // With tau <= 0 every new row max moves the reference, so P is formed
+        // after the row maxima (MAXFIRST), the classic order.
         const float tau_pow = __builtin_amdgcn_exp2f(tau) * 0.999f;
-        auto softmax = [&](int t, auto MASKC) __attribute__((always_inline)) {
+        auto softmax = [&](int t, auto MASKC, auto MAXFIRSTC) __attribute__((always_inline)) {
+            constexpr bool MAXFIRST = decltype(MAXFIRSTC)::value;
             const int kv0 = t * kBc;
             if constexpr (decltype(MASKC)::value) {
 #pragma unroll
@@ -328,25 +331,35 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(
             // of the rows whose max exceeds it by more than tau, and form P
             // again for a half in which any row moved.
             float part[2], alpha[2] = {1.0f, 1.0f};
+            // row max over this lane's 32 keys, then across the half-waves;
+            // moves the reference of the rows whose max exceeds it by more
+            // than tau
+            auto move_reference = [&](int sb) __attribute__((always_inline)) {
+                float mx = sacc[sb][0][0];
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb) part[sb] = form_p(sb, -m_ref[sb]);
-            if (__builtin_amdgcn_ballot_w64(!(part[0] <= tau_pow) || !(part[1] <= tau_pow))) {
+                for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[sb][0][r]);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][1][r]);
+                mx = max_halves(mx);
+                const float m_new = mx * c;
+                const bool need = m_new > m_ref[sb] + tau;
+                alpha[sb] = need ? __builtin_amdgcn_exp2f(m_ref[sb] - m_new) : 1.0f;
+                m_ref[sb] = need ? m_new : m_ref[sb];
+                return need;
+            };
+            if constexpr (MAXFIRST) {
 #pragma unroll
                 for (int sb = 0; sb < 2; ++sb) {
-                    // row max over this lane's 32 keys, then across the half-waves
-                    float mx = sacc[sb][0][0];
+                    move_reference(sb);
+                    part[sb] = form_p(sb, -m_ref[sb]);
+                }
+            } else {
 #pragma unroll
-                    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[sb][0][r]);
+                for (int sb = 0; sb < 2; ++sb) part[sb] = form_p(sb, -m_ref[sb]);
+                if (__builtin_amdgcn_ballot_w64(!(part[0] <= tau_pow) || !(part[1] <= tau_pow))) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][1][r]);
-                    mx = max_halves(mx);
-                    const float m_new = mx * c;
-                    const bool need = m_new > m_ref[sb] + tau;
-                    if (__builtin_amdgcn_ballot_w64(need)) {
-                        alpha[sb] = need ? __builtin_amdgcn_exp2f(m_ref[sb] - m_new) : 1.0f;
-                        m_ref[sb] = need ? m_new : m_ref[sb];
-                        part[sb] = form_p(sb, -m_ref[sb]);
-                    }
+                    for (int sb = 0; sb < 2; ++sb)
+                        if (__builtin_amdgcn_ballot_w64(move_reference(sb))) part[sb] = form_p(sb, -m_ref[sb]);
                 }
             }
 #pragma unroll
@@ -357,19 +370,25 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(
         };
 
         // Iteration j: S^T(j), then its softmax.
-        auto iteration = [&](int j, auto MASKC) __attribute__((always_inline)) {
+        auto iteration = [&](int j, auto MASKC, auto MAXFIRSTC) __attribute__((always_inline)) {
             if (j + 1 < nkv) issue_k(j + 1);
             if (j < nkv) issue_v(j);
             if (j < nkv) {
                 s_product(j);
-                softmax(j, MASKC);
+                softmax(j, MASKC, MAXFIRSTC);
             }
             wait_vmem();
             __syncthreads();
         };
-        int j = 0;
-        for (; j < n_plain; ++j) iteration(j, std::false_type{});
-        for (; j <= nkv; ++j) iteration(j, std::true_type{});
+        auto tiles = [&](auto MAXFIRSTC) __attribute__((always_inline)) {
+            int j = 0;
+            for (; j < n_plain; ++j) iteration(j, std::false_type{}, MAXFIRSTC);
+            for (; j <= nkv; ++j) iteration(j, std::true_type{}, MAXFIRSTC);
+        };
+        if (tau > 0.0f)
+            tiles(std::false_type{});
+        else
+            tiles(std::true_type{});
 
         // hand the row sums and reference maxima to the PV wave; store LSE
         const fa_rsrc rL = make_rsrc(LSE + lse0, (uint32_t)S * 4);

@@ -22,10 +22,11 @@
 //
 // dK/dV kernel: one workgroup = 8 waves = 128 key rows; each pair of waves
 // (one per SIMD half) owns 32 keys and splits every 64-row query block in
-// two, so each SIMD holds two waves that overlap MFMA with softmax work.  K
-// and V of the block stay in LDS, dK and dV accumulate in registers; query
-// blocks (Q, dO, LSE, D) stream through a double-buffered LDS stage filled by
-// direct memory-to-LDS copies.  Per wave and block: S = Q K^T and
+// two, so each SIMD holds two waves that overlap MFMA with softmax work.  V
+// of the block stays in LDS, each wave's K rows are read into registers
+// once, dK and dV accumulate in registers; query blocks (Q, dO, LSE, D)
+// stream through a double-buffered LDS stage filled by direct memory-to-LDS
+// copies.  Per wave and block: S = Q K^T and
 // dP = dO V^T (keys on the lanes), P and dS in registers, dV += P^T dO and
 // dK += dS^T Q with P and dS fed straight from the accumulators and dO, Q
 // through transposing LDS reads.
@@ -181,6 +182,11 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
             for (int s2 = 0; s2 < 2; ++s2)
                 troff[db][s2] = tile_off<NCH>(32 * qh + 4 * h + 8 * s2 + (L >> 2), (32 * db + col) * 2);
     }
+    // This wave's K rows (B operands of S = Q K^T) are the same for every
+    // query block: read them from LDS once.
+    fa_u32x4 kreg[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kreg[ks] = lds_read16(sK, koff[ks]);
 
     // One query block.  MASK: causal blocks that cross this key block's
     // diagonal.  Keys at or past S need no mask here: they only feed dK, dV
@@ -196,7 +202,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
         fa_f32x16 sacc = zero16(), pacc = zero16();
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            sacc = mfma32(lds_read16(sQ, qoff[ks]), lds_read16(sK, koff[ks]), sacc);
+            sacc = mfma32(lds_read16(sQ, qoff[ks]), kreg[ks], sacc);
             pacc = mfma32(lds_read16(sO, qoff[ks]), lds_read16(sV, koff[ks]), pacc);
         }
 

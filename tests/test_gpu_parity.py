@@ -317,6 +317,34 @@ def test_workload_backward_sampled(fa, name, causal):
     check_grad(bf16_to_np64(dv[b, h, cidx]), gv, f"{name} dV cols")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_head_dim_64_sampled(fa, causal):
+    """d = 64 at a multi-tile size with a ragged tail (B=2, H=3, S=3000):
+    sampled forward rows, dQ rows, dK/dV columns of two heads against the
+    oracle."""
+    B, H, S, d = 2, 3, 3000, 64
+    say(f"[d=64] B={B} H={H} S={S} causal={causal}")
+    shape = (B, H, S, d)
+    qb, kb, vb, dob = (rand_bits(shape, 7500 + i) for i in range(4))
+    scale = 1.0 / np.sqrt(d)
+    q, k, v, o, lse = run_fwd(fa, qb, kb, vb, causal, scale)
+    dq, dk, dv = fa.backward(q, k, v, o, lse, to_dev(dob), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    rows = sample_rows(S)
+    cols = np.array(sorted({0, 1, 127, 128, S // 3, S // 2, S - 129, S - 128, S - 1}), dtype=np.int64)
+    idx, cidx = torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        Q, K, V, dO = (gen.bf16_bits_to_f64(x[b, h]) for x in (qb, kb, vb, dob))
+        o_ref, l_ref = oracle.forward_rows(Q, K, V, rows, scale, causal)
+        check_o(bf16_to_np64(o[b, h, idx]), o_ref, f"d=64 O rows head ({b},{h})")
+        check_lse(lse[b, h, idx].cpu().numpy().astype(np.float64), l_ref, f"d=64 LSE rows head ({b},{h})")
+        gq = oracle.backward_dq_rows(Q, K, V, dO, rows, scale, causal)
+        check_grad(dq[b, h, idx].cpu().numpy().astype(np.float64), gq, f"d=64 dQ rows head ({b},{h})")
+        gk, gv = oracle.backward_dkdv_cols(Q, K, V, dO, cols, scale, causal)
+        check_grad(bf16_to_np64(dk[b, h, cidx]), gk, f"d=64 dK cols head ({b},{h})")
+        check_grad(bf16_to_np64(dv[b, h, cidx]), gv, f"d=64 dV cols head ({b},{h})")
+
+
 def test_backward_is_bitwise_repeatable(fa):
     """Every gradient element is written once (no atomics): two runs agree bit for bit."""
     say("[determinism] backward twice")

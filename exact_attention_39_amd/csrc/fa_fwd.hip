@@ -458,20 +458,30 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(
         }
         __syncthreads();  // the score wave's row sums are in the buffer
 
-        // Epilogue: normalise, store O (bf16).
-        const fa_rsrc rO = make_rsrc(O + head, head_bytes);
+        // Epilogue: normalise O (bf16) into this wave's 64 rows of a
+        // swizzled LDS tile (the K/V slots are free now), then store whole
+        // rows: each lane holds 4 consecutive d of a column of O^T, so
+        // stores straight from the accumulators would touch 32 rows per
+        // instruction with 8 bytes each.
+        fa_lds_char *sO = smem + (w - 4) * (64 * ROWB);
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             const float inv = 1.0f / *(const __attribute__((address_space(3))) float *)a_slot(0, sb);
-            const int qrow = prow0 + 32 * sb + n;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     fa_u32x2 v = {pack_bf16(oacc[sb][db][4 * g] * inv, oacc[sb][db][4 * g + 1] * inv),
                                   pack_bf16(oacc[sb][db][4 * g + 2] * inv, oacc[sb][db][4 * g + 3] * inv)};
-                    buf_store8(rO, (uint32_t)qrow * pitch + (32 * db + 8 * g + 4 * h) * 2, v);
+                    lds_write8(sO, tile_off<NCH>(32 * sb + n, (32 * db + 8 * g + 4 * h) * 2), v);
                 }
+        }
+        const fa_rsrc rO = make_rsrc(O + head, head_bytes);
+        constexpr int RPI = 1024 / ROWB;  // rows per 1 KB store instruction
+#pragma unroll
+        for (int i = 0; i < 64 / RPI; ++i) {
+            const int row = i * RPI + lane / NCH, ch = lane % NCH;
+            buf_store16(rO, (uint32_t)(prow0 + row) * pitch + ch * 16, lds_read16(sO, tile_off<NCH>(row, ch * 16)));
         }
     }
 }

@@ -435,15 +435,28 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     for (int j = n_plain; j < nkv; ++j) step(j, std::true_type{});
 
     // Epilogue: lane = query row, registers = 4 consecutive d per group.
-    const fa_rsrc rdQ = make_rsrc(dQ + head, (uint32_t)S * D * 4);
+    // The scaled rows go through LDS (the K/V stages are free: every wave
+    // has passed the last barrier), 16-byte chunk index XORed with the row,
+    // and leave as whole rows; stored straight from the accumulators, each
+    // instruction would touch 32 rows with 32 bytes each.
+    constexpr int RB4 = D * 4, NC4 = RB4 / 16;
+    fa_lds_char *sQd = smem + w * (32 * RB4);
+    auto off4 = [&](int row, int ch) { return row * RB4 + ((ch ^ (row & (NC4 - 1))) << 4); };
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             fa_u32x4 v = {__float_as_uint(dqacc[db][4 * g] * scale), __float_as_uint(dqacc[db][4 * g + 1] * scale),
                           __float_as_uint(dqacc[db][4 * g + 2] * scale), __float_as_uint(dqacc[db][4 * g + 3] * scale)};
-            buf_store16(rdQ, ((uint32_t)qrow * D + 32 * db + 8 * g + 4 * h) * 4, v);
+            lds_write16(sQd, off4(n, 8 * db + 2 * g + h), v);
         }
+    const fa_rsrc rdQ = make_rsrc(dQ + head, (uint32_t)S * D * 4);
+    constexpr int RPI = 1024 / RB4;  // rows per 1 KB store instruction
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+        const int row = i * RPI + lane / NC4, ch = lane % NC4;
+        buf_store16(rdQ, (uint32_t)(wq_lo + row) * RB4 + ch * 16, lds_read16(sQd, off4(row, ch)));
+    }
 }
 
 template <int D>

@@ -20,16 +20,16 @@
 // instead of 5) but writes dQ once with plain stores.  The backward is then
 // free of atomics and bitwise deterministic.
 //
-// dK/dV kernel: one workgroup = 8 waves = 128 key rows; each pair of waves
-// (one per SIMD half) owns 32 keys and splits every 64-row query block in
-// two, so each SIMD holds two waves that overlap MFMA with softmax work.  V
-// of the block stays in LDS, each wave's K rows are read into registers
-// once, dK and dV accumulate in registers; query blocks (Q, dO, LSE, D)
-// stream through a double-buffered LDS stage filled by direct memory-to-LDS
-// copies.  Per wave and block: S = Q K^T and
-// dP = dO V^T (keys on the lanes), P and dS in registers, dV += P^T dO and
-// dK += dS^T Q with P and dS fed straight from the accumulators and dO, Q
-// through transposing LDS reads.
+// dK/dV kernel: one workgroup = 8 waves = 256 key rows; each wave owns 32
+// keys and takes the two 32-row halves of every 64-row query block in turn,
+// two waves per SIMD overlapping MFMA with softmax work.  V of the block
+// stays in LDS, each wave's K rows sit in registers (loaded once), dK and dV
+// accumulate in registers; query blocks (Q, dO, LSE, D) stream through a
+// double-buffered LDS stage filled by direct memory-to-LDS copies, one
+// barrier per 64 queries x 256 keys.  Per wave and half block: S = Q K^T
+// and dP = dO V^T (keys on the lanes), P and dS in registers, dV += P^T dO
+// and dK += dS^T Q with P and dS fed straight from the accumulators and dO,
+// Q through transposing LDS reads.
 //
 // dQ kernel: one workgroup = 4 waves = 128 query rows (32 per wave), two
 // workgroups per CU; Q and dO rows resident as B operands, keys/values
@@ -51,7 +51,6 @@ namespace fa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kKvPerBlock = 128;  // dK/dV kernel: key rows per workgroup
 constexpr int kQPerIter = 64;     // dK/dV kernel: query rows per iteration
 constexpr int kQPerBlock = 128;   // dQ kernel: query rows per workgroup
 constexpr int kKvPerTile = 64;    // dQ kernel: key rows per tile
@@ -87,10 +86,11 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const uint16_t *__res
 }
 
 // ---------------------------------------------------------------- dK, dV
-// 8 waves: wave w owns keys 32 (w % 4) .. +31 of the block and query half
-// w / 4 of every 64-row query block, so two waves on each SIMD interleave.
-// K and V of the block sit in LDS; the two waves that share keys add their
-// dK, dV partials through LDS once, at the end.
+// 8 waves, 256 keys: wave w owns keys 32 w .. +31 of the block and takes the
+// two 32-row halves of every 64-row query block in turn.  (Against 128 keys
+// per workgroup with the query halves on the two waves of a SIMD: half the
+// barriers and stage copies per MFMA, and no dK/dV exchange at the end.)
+constexpr int kKB = 256;
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
@@ -102,31 +102,25 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
     constexpr int QTILE = kQPerIter * ROWB;
-    constexpr int KTILE = kKvPerBlock * ROWB;
-    constexpr int SMEM = 2 * KTILE + 4 * QTILE + 4 * kQPerIter * 4;
-    static_assert(SMEM >= 4 * 2 * DB * 16 * 64 * 4, "epilogue exchange must fit in LDS");
+    constexpr int VTILE = kKB * ROWB;
+    constexpr int SMEM = VTILE + 4 * QTILE + 4 * kQPerIter * 4;
 
     __shared__ __attribute__((aligned(1024))) char smem_raw[SMEM];
     fa_lds_char *smem = (fa_lds_char *)smem_raw;
-    fa_lds_char *sK = smem;                      // K rows of the block
-    fa_lds_char *sV = sK + KTILE;                // V rows of the block
-    fa_lds_char *sQ0 = sV + KTILE;               // [2] Q tiles
+    fa_lds_char *sV = smem;                      // V rows of the block
+    fa_lds_char *sQ0 = sV + VTILE;               // [2] Q tiles
     fa_lds_char *sO0 = sQ0 + 2 * QTILE;          // [2] dO tiles
     fa_lds_char *sLD = sO0 + 2 * QTILE;          // [2][LSE 64 | D 64] floats
 
     const int lane = threadIdx.x & 63, w = wave_id();
     const int h = lane >> 5, n = lane & 31;
-    const int kw = w & 3;   // key slice of this wave
-    const int qh = w >> 2;  // query half of this wave
 
     const int bh = blockIdx.x % BH;
-    // causal: key block 0 meets the most query blocks, so ascending ids run
-    // longest first; lpt == 0 reverses the order (for measurement)
-    const int kblk = (CAUSAL && !lpt) ? ((S + kKvPerBlock - 1) / kKvPerBlock - 1 - (int)(blockIdx.x / BH))
-                                      : (int)(blockIdx.x / BH);
-    const int k0 = kblk * kKvPerBlock;
+    const int nkb = (S + kKB - 1) / kKB;
+    const int kblk = (CAUSAL && !lpt) ? (nkb - 1 - (int)(blockIdx.x / BH)) : (int)(blockIdx.x / BH);
+    const int k0 = kblk * kKB;
     const size_t head = (size_t)bh * (size_t)S * D;
-    const int kv = k0 + 32 * kw + n;  // this lane's key for S and dP
+    const int kv = k0 + 32 * w + n;  // this lane's key for S and dP
 
     const uint32_t head_bytes = (uint32_t)S * ROWB;
     const fa_rsrc rQ = make_rsrc(Q + head, head_bytes);
@@ -134,8 +128,14 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
     const fa_rsrc rL = make_rsrc(L2vec + (size_t)bh * S, (uint32_t)S * 4);
     const fa_rsrc rD = make_rsrc(Dvec + (size_t)bh * S, (uint32_t)S * 4);
 
-    tile_to_lds<NCH, kKvPerBlock, NW>(make_rsrc(K + head, head_bytes), k0, sK, w, lane);
-    tile_to_lds<NCH, kKvPerBlock, NW>(make_rsrc(V + head, head_bytes), k0, sV, w, lane);
+    tile_to_lds<NCH, kKB, NW>(make_rsrc(V + head, head_bytes), k0, sV, w, lane);
+    // this wave's K rows, the B operands of S = Q K^T, straight to registers
+    fa_u32x4 kreg[KS];
+    {
+        const fa_rsrc rK = make_rsrc(K + head, head_bytes);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kreg[ks] = buf_load16(rK, (uint32_t)kv * ROWB + (16 * ks + 8 * h) * 2);
+    }
 
     fa_f32x16 dkacc[DB], dvacc[DB];
 #pragma unroll
@@ -147,9 +147,6 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
     const int nqb = (S + kQPerIter - 1) / kQPerIter;
     const int ib = CAUSAL ? k0 / kQPerIter : 0;
 
-    // Query block i -> LDS stage: Q and dO tiles (all waves), LSE (wave 0)
-    // and D (wave 1).  Rows past S arrive as zeros; such rows then carry
-    // dO = 0 and D = 0, so they add nothing to dV or dK.
     auto issue = [&](int i, int buf) {
         tile_to_lds<NCH, kQPerIter, NW>(rQ, i * kQPerIter, sQ0 + buf * QTILE, w, lane);
         tile_to_lds<NCH, kQPerIter, NW>(rdO, i * kQPerIter, sO0 + buf * QTILE, w, lane);
@@ -163,16 +160,13 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
     wait_vmem();
     __syncthreads();
 
-    // Lane-dependent LDS offsets, computed once (see the forward kernel):
-    // row reads of query row 32 qh + n and key row 32 kw + n at chunk
-    // 2 ks + h, and transposing reads of query rows 32 qh + 16 t + 4 h +
-    // 8 s + L/4 (t is an immediate).
-    int qoff[KS], koff[KS], troff[DB][2];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        qoff[ks] = tile_off<NCH>(32 * qh + n, (2 * ks + h) * 16);
-        koff[ks] = tile_off<NCH>(32 * kw + n, (2 * ks + h) * 16);
-    }
+    // Lane-dependent LDS offsets within query half 0 (half 1 is 32 rows,
+    // a multiple of the swizzle period, further on) and of this wave's V rows.
+    // The swizzle XORs the chunk index, so the offset of k-step ks is the
+    // offset of k-step 0 with 2 ks XORed into the chunk bits.
+    int troff[DB][2];
+    const int qoff0 = tile_off<NCH>(n, h * 16);
+    const int voff0 = tile_off<NCH>(32 * w + n, h * 16);
     {
         const int L = lane & 15;
         const int col = ((lane >> 4) & 1) * 16 + (L & 3) * 4;
@@ -180,38 +174,32 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
-                troff[db][s2] = tile_off<NCH>(32 * qh + 4 * h + 8 * s2 + (L >> 2), (32 * db + col) * 2);
+                troff[db][s2] = tile_off<NCH>(4 * h + 8 * s2 + (L >> 2), (32 * db + col) * 2);
     }
-    // This wave's K rows (B operands of S = Q K^T) are the same for every
-    // query block: read them from LDS once.
-    fa_u32x4 kreg[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kreg[ks] = lds_read16(sK, koff[ks]);
 
-    // One query block.  MASK: causal blocks that cross this key block's
-    // diagonal.  Keys at or past S need no mask here: they only feed dK, dV
-    // rows that are never stored.
-    auto compute_block = [&](int buf, int q0, auto MASKC) {
+    auto compute_half = [&](int buf, int q0, auto QHC, auto MASKC) {
+        constexpr int qh = decltype(QHC)::value;
         constexpr bool MASK = decltype(MASKC)::value;
-        const fa_lds_char *sQ = sQ0 + buf * QTILE;
-        const fa_lds_char *sO = sO0 + buf * QTILE;
-        const fa_lds_char *sL = sLD + buf * 2 * kQPerIter * 4;
+        const fa_lds_char *sQ = sQ0 + buf * QTILE + qh * 32 * ROWB;
+        const fa_lds_char *sO = sO0 + buf * QTILE + qh * 32 * ROWB;
+        const fa_lds_char *sL = sLD + buf * 2 * kQPerIter * 4 + qh * 32 * 4;
         const fa_lds_char *sD = sL + kQPerIter * 4;
 
-        // S = Q K^T and dP = dO V^T: this wave's 32 queries x its 32 keys.
+        // fresh copies per half, so that the eight offsets are formed at
+        // their reads rather than hoisted out of the loop into registers
+        int qb = qoff0, vb = voff0;
+        asm volatile("" : "+v"(qb), "+v"(vb));
         fa_f32x16 sacc = zero16(), pacc = zero16();
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            sacc = mfma32(lds_read16(sQ, qoff[ks]), kreg[ks], sacc);
-            pacc = mfma32(lds_read16(sO, qoff[ks]), lds_read16(sV, koff[ks]), pacc);
+            const int qo = qb ^ (ks << 5);
+            sacc = mfma32(lds_read16(sQ, qo), kreg[ks], sacc);
+            pacc = mfma32(lds_read16(sO, qo), lds_read16(sV, vb ^ (ks << 5)), pacc);
         }
-
-        // P = 2^(s c - LSE log2 e) (masked -> 0), dS = P (dP - D); the
-        // factor scale of dS is applied to dK once, at the end.
         fa_u32x4 pf[2], dsf[2];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const int qi = 32 * qh + 8 * g + 4 * h;
+            const int qi = 8 * g + 4 * h;
             const fa_f32x4 l4 = *(const __attribute__((address_space(3))) fa_f32x4 *)(sL + qi * 4);
             const fa_f32x4 d4 = *(const __attribute__((address_space(3))) fa_f32x4 *)(sD + qi * 4);
             float p[4], ds[4];
@@ -219,7 +207,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * g + e;
                 float pv = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, -l4[e]));
-                if constexpr (MASK) pv = kv > q0 + qi + e ? 0.0f : pv;
+                if constexpr (MASK) pv = kv > q0 + 32 * qh + qi + e ? 0.0f : pv;
                 p[e] = pv;
                 ds[e] = pv * (pacc[r] - d4[e]);
             }
@@ -230,9 +218,6 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
             dsf[t][wd] = pack_bf16(ds[0], ds[1]);
             dsf[t][wd + 1] = pack_bf16(ds[2], ds[3]);
         }
-
-        // dV += P^T dO and dK += dS^T Q over this wave's 32 queries; query
-        // order of k-step t follows the accumulator rows 16t + 8(j/4) + 4h + j%4.
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -252,44 +237,27 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
     auto step = [&](int i, auto MASKC) {
         const int buf = (i - ib) & 1;
         if (i + 1 < nqb) issue(i + 1, buf ^ 1);
-        compute_block(buf, i * kQPerIter, MASKC);
-        wait_vmem();      // next query block has landed
-        __syncthreads();  // ... for every wave, and this block's stage is free
+        compute_half(buf, i * kQPerIter, std::integral_constant<int, 0>{}, MASKC);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_half(buf, i * kQPerIter, std::integral_constant<int, 1>{}, MASKC);
+        wait_vmem();
+        __syncthreads();
     };
 
-    // causal: the first two query blocks cross the diagonal of this key block
-    const int i_plain = CAUSAL ? min(nqb, (k0 + kKvPerBlock - 1) / kQPerIter + 1) : ib;
+    const int i_plain = CAUSAL ? min(nqb, (k0 + kKB - 1) / kQPerIter + 1) : ib;
     for (int i = ib; i < i_plain; ++i) step(i, std::true_type{});
     for (int i = i_plain; i < nqb; ++i) step(i, std::false_type{});
 
-    // Epilogue: the upper query half hands its partials to the lower half
-    // through LDS (all stages are free now), which adds and stores.
-    // Layout per key slice kw: [dV | dK][db][r][lane] fp32.
-    fa_lds_char *xch = smem + kw * (2 * DB * 16 * 64 * 4);
-    if (qh == 1) {
+    const fa_rsrc rdK = make_rsrc(dK + head, head_bytes);
+    const fa_rsrc rdV = make_rsrc(dV + head, head_bytes);
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                *(__attribute__((address_space(3))) float *)(xch + (((0 * DB + db) * 16 + r) * 64 + lane) * 4) = dvacc[db][r];
-                *(__attribute__((address_space(3))) float *)(xch + (((1 * DB + db) * 16 + r) * 64 + lane) * 4) = dkacc[db][r];
-            }
-    }
-    __syncthreads();
-    if (qh == 0) {
-        const fa_rsrc rdK = make_rsrc(dK + head, head_bytes);
-        const fa_rsrc rdV = make_rsrc(dV + head, head_bytes);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float v = dvacc[db][r] + *(const __attribute__((address_space(3))) float *)(xch + (((0 * DB + db) * 16 + r) * 64 + lane) * 4);
-                const float k = (dkacc[db][r] + *(const __attribute__((address_space(3))) float *)(xch + (((1 * DB + db) * 16 + r) * 64 + lane) * 4)) * scale;
-                const int kr = k0 + 32 * kw + 8 * (r >> 2) + 4 * h + (r & 3);
-                const uint32_t off = ((uint32_t)kr * D + 32 * db + n) * 2;
-                buf_store2(rdK, off, (uint16_t)(pack_bf16(k, 0.0f) & 0xFFFFu));
-                buf_store2(rdV, off, (uint16_t)(pack_bf16(v, 0.0f) & 0xFFFFu));
-            }
+        for (int r = 0; r < 16; ++r) {
+            const int kr = k0 + 32 * w + 8 * (r >> 2) + 4 * h + (r & 3);
+            const uint32_t off = ((uint32_t)kr * D + 32 * db + n) * 2;
+            buf_store2(rdK, off, (uint16_t)(pack_bf16(dkacc[db][r] * scale, 0.0f) & 0xFFFFu));
+            buf_store2(rdV, off, (uint16_t)(pack_bf16(dvacc[db][r], 0.0f) & 0xFFFFu));
         }
     }
 }
@@ -471,7 +439,7 @@ hipError_t launch_pre_d(const BwdArgs &a, hipStream_t st) {
 
 template <int D, bool CAUSAL>
 hipError_t launch_dkdv_t(const BwdArgs &a, hipStream_t st) {
-    const int nkb = (a.S + kKvPerBlock - 1) / kKvPerBlock;
+    const int nkb = (a.S + kKB - 1) / kKB;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(a.BH * nkb)), dim3(2 * kThreads), 0, st,
                        (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
                        (const float *)a.Dvec + (size_t)a.BH * a.S, (const float *)a.Dvec,

@@ -34,10 +34,11 @@
 //     and P may reach 2^tau (gist.science German explainer, section 3: skip
 //     the rescale when the numbers do not grow too large).  The decision is
 //     per row, the multiply is skipped for the whole wave when no row needs
-//     it.  The result does not depend on tau beyond rounding.  P is formed
-//     against the reference first; the row maxima are only taken when some
-//     lane's partial row sum exceeds 2^tau (then some P may have), which
-//     leaves the common tile with no max reduction at all;
+//     it.  The result does not depend on tau beyond rounding.  With tau > 0
+//     P is formed against the reference first and the row maxima are only
+//     taken when some lane's partial row sum exceeds 2^tau (then some P may
+//     have), which leaves the common tile with no max reduction at all;
+//     tau <= 0 takes the maxima first (the classic order);
 //   * hybrid exp2: POLY eighths of the exponentials (a static subset of the
 //     registers) use the FMA polynomial of exp2_poly.h, the rest v_exp_f32
 //     (technical summary, methodology item 2);

@@ -18,6 +18,7 @@ import numpy as np
 import pytest
 
 import attn_inputs as gen
+import golden_worked
 import oracle
 
 torch = pytest.importorskip("torch")
@@ -121,6 +122,25 @@ def test_small_forward_backward_full_tensors(fa, B, H, S, d, causal):
     check_grad(dq.cpu().numpy().astype(np.float64), gq, "dQ")
     check_grad(bf16_to_np64(dk), gk, "dK")
     check_grad(bf16_to_np64(dv), gv, "dV")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_hand_worked_examples(fa, d):
+    """The hand-derived closed forms of tests/golden/hand_worked_examples.json,
+    padded to head dimension d; every input value is exact in bf16."""
+    for c in golden_worked.cases(d):
+        say(f"[golden] {c['name']} d={d}")
+        bits = {t: gen.f32_to_bf16_bits(c[t].astype(np.float32))[None, None] for t in ("q", "k", "v", "do")}
+        for t, b in bits.items():
+            assert np.array_equal(gen.bf16_bits_to_f64(b)[0, 0], c[t]), (c["name"], t)
+        q, k, v, o, lse = run_fwd(fa, bits["q"], bits["k"], bits["v"], c["causal"], c["scale"])
+        check_o(bf16_to_np64(o)[0, 0], c["o"], c["name"])
+        check_lse(lse.cpu().numpy().astype(np.float64)[0, 0], c["lse"], c["name"])
+        dq, dk, dv = fa.backward(q, k, v, o, lse, to_dev(bits["do"]), causal=c["causal"], scale=c["scale"])
+        torch.cuda.synchronize()
+        check_grad(dq.cpu().numpy().astype(np.float64)[0, 0], c["dq"], c["name"] + " dQ")
+        check_grad(bf16_to_np64(dk)[0, 0], c["dk"], c["name"] + " dK")
+        check_grad(bf16_to_np64(dv)[0, 0], c["dv"], c["name"] + " dV")
 
 
 def test_smoke_workload_forward(fa):

@@ -16,7 +16,10 @@ one of them:
 * central finite differences of L = sum(dO * O) for all three gradients;
 * gradient identities: dQ = 0 when all keys are equal, dK = 0 and dV uniform
   when Q = 0, linearity of every gradient in dO;
-* the sampled-row / sampled-column entry points equal the full ones.
+* the sampled-row / sampled-column entry points equal the full ones;
+* hand-worked examples (tests/golden/hand_worked_examples.json): scores that
+  are logarithms of small integers, so that P, O, LSE and every gradient are
+  simple closed forms derived by hand in that file.
 
 The pages print no worked example, so no fixture value comes from them.
 """
@@ -26,6 +29,7 @@ import numpy as np
 import pytest
 
 import attn_inputs as gen
+import golden_worked
 import oracle
 
 rng = np.random.default_rng(1234)
@@ -278,3 +282,13 @@ def test_normal_draws_are_standard_normal():
     # chunked generation is the same stream as one shot
     y = gen.normal_f32(0xFA000010, 1001, chunk=100)
     np.testing.assert_array_equal(y, gen.normal_f32(0xFA000010, 1001))
+
+
+# ------------------------------------------------------- hand-worked examples
+@pytest.mark.parametrize("d", [2, 5])
+def test_hand_worked_examples(d):
+    for c in golden_worked.cases(d):
+        o, lse = oracle.attention_forward(c["q"], c["k"], c["v"], c["scale"], c["causal"])
+        dq, dk, dv = oracle.attention_backward(c["q"], c["k"], c["v"], c["do"], c["scale"], c["causal"])
+        for got, t in ((o, "o"), (lse, "lse"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+            assert np.abs(got - c[t]).max() <= 1e-13, (c["name"], t, got, c[t])

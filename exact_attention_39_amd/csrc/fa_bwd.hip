@@ -60,8 +60,10 @@ template <bool WIDE> constexpr int kDqWaves = WIDE ? 8 : 4;
 template <bool WIDE> constexpr int kQPerBlock = 32 * kDqWaves<WIDE>;
 template <bool WIDE> constexpr int kKvPerTile = WIDE ? 128 : 64;
 
-// D_i = sum_k dO_ik O_ik and LSE_i * log2(e) (the base-2 exponent offset the
-// two gradient kernels use), both into the workspace.
+// -D_i = -sum_k dO_ik O_ik and LSE_i * log2(e) (the base-2 exponent offset
+// the two gradient kernels use), both into the workspace.  D is kept negated
+// so that the dK/dV kernel can start its dP accumulators at -D and take
+// dS = P (dP - D) straight from them.
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const uint16_t *__restrict__ O,
                                                            const uint16_t *__restrict__ dO,
@@ -85,7 +87,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const uint16_t *__res
 #pragma unroll
     for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
     if (row < rows && part == 0) {
-        Dvec[row] = acc;
+        Dvec[row] = -acc;
         L2vec[row] = LSE[row] * FA_LOG2E;
     }
 }
@@ -108,14 +110,19 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
     constexpr int DB = D / 32;
     constexpr int QTILE = kQPerIter * ROWB;
     constexpr int VTILE = kKB * ROWB;
-    constexpr int SMEM = VTILE + 4 * QTILE + 4 * kQPerIter * 4;
+    constexpr int LDB = 4 * kQPerIter * 4;
+    constexpr int SMEM = LDB + 4 * QTILE + VTILE;
 
+    // The query-side stages come first, so that each of their reads is one
+    // register (lane offset with the stage folded in, flipped once per
+    // iteration) plus an immediate below 64 KB, the reach of the LDS
+    // instructions' offset field: no address arithmetic per read.
     __shared__ __attribute__((aligned(1024))) char smem_raw[SMEM];
     fa_lds_char *smem = (fa_lds_char *)smem_raw;
-    fa_lds_char *sV = smem;                      // V rows of the block
-    fa_lds_char *sQ0 = sV + VTILE;               // [2] Q tiles
+    fa_lds_char *sLD = smem;                     // [2][LSE 64 | D 64] floats
+    fa_lds_char *sQ0 = sLD + LDB;                // [2] Q tiles
     fa_lds_char *sO0 = sQ0 + 2 * QTILE;          // [2] dO tiles
-    fa_lds_char *sLD = sO0 + 2 * QTILE;          // [2][LSE 64 | D 64] floats
+    fa_lds_char *sV = sO0 + 2 * QTILE;           // V rows of the block
 
     const int lane = threadIdx.x & 63, w = wave_id();
     const int h = lane >> 5, n = lane & 31;
@@ -168,10 +175,13 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
     // Lane-dependent LDS offsets within query half 0 (half 1 is 32 rows,
     // a multiple of the swizzle period, further on) and of this wave's V rows.
     // The swizzle XORs the chunk index, so the offset of k-step ks is the
-    // offset of k-step 0 with 2 ks XORed into the chunk bits.
+    // offset of k-step 0 with 2 ks XORed into the chunk bits.  The query-side
+    // offsets (< QTILE / 2) carry the stage as bit QTILE, flipped after every
+    // iteration; the LSE/D offset carries it as bit 2 * kQPerIter * 4.
     int troff[DB][2];
-    const int qoff0 = tile_off<NCH>(n, h * 16);
-    const int voff0 = tile_off<NCH>(32 * w + n, h * 16);
+    int qoff = tile_off<NCH>(n, h * 16);
+    const int voff0 = (int)(sV - smem) + tile_off<NCH>(32 * w + n, h * 16);
+    int ldoff = 16 * h;
     {
         const int L = lane & 15;
         const int col = ((lane >> 4) & 1) * 16 + (L & 3) * 4;
@@ -182,31 +192,37 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
                 troff[db][s2] = tile_off<NCH>(4 * h + 8 * s2 + (L >> 2), (32 * db + col) * 2);
     }
 
-    auto compute_half = [&](int buf, int q0, auto QHC, auto MASKC) {
+    auto compute_half = [&](int q0, auto QHC, auto MASKC) {
         constexpr int qh = decltype(QHC)::value;
         constexpr bool MASK = decltype(MASKC)::value;
-        const fa_lds_char *sQ = sQ0 + buf * QTILE + qh * 32 * ROWB;
-        const fa_lds_char *sO = sO0 + buf * QTILE + qh * 32 * ROWB;
-        const fa_lds_char *sL = sLD + buf * 2 * kQPerIter * 4 + qh * 32 * 4;
+        const fa_lds_char *sQ = sQ0 + qh * 32 * ROWB;
+        const fa_lds_char *sO = sO0 + qh * 32 * ROWB;
+        const fa_lds_char *sL = sLD + qh * 32 * 4 + ldoff;
         const fa_lds_char *sD = sL + kQPerIter * 4;
 
         // fresh copies per half, so that the eight offsets are formed at
         // their reads rather than hoisted out of the loop into registers
-        int qb = qoff0, vb = voff0;
+        int qb = qoff, vb = voff0;
         asm volatile("" : "+v"(qb), "+v"(vb));
-        fa_f32x16 sacc = zero16(), pacc = zero16();
+        // dP accumulates on top of -D of its query row, so it ends as dP - D
+        fa_f32x16 sacc = zero16(), pacc;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const fa_f32x4 nd4 = *(const __attribute__((address_space(3))) fa_f32x4 *)(sD + 32 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pacc[4 * g + e] = nd4[e];
+        }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int qo = qb ^ (ks << 5);
             sacc = mfma32(lds_read16(sQ, qo), kreg[ks], sacc);
-            pacc = mfma32(lds_read16(sO, qo), lds_read16(sV, vb ^ (ks << 5)), pacc);
+            pacc = mfma32(lds_read16(sO, qo), lds_read16(smem, vb ^ (ks << 5)), pacc);
         }
         fa_u32x4 pf[2], dsf[2];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int qi = 8 * g + 4 * h;
-            const fa_f32x4 l4 = *(const __attribute__((address_space(3))) fa_f32x4 *)(sL + qi * 4);
-            const fa_f32x4 d4 = *(const __attribute__((address_space(3))) fa_f32x4 *)(sD + qi * 4);
+            const fa_f32x4 l4 = *(const __attribute__((address_space(3))) fa_f32x4 *)(sL + 32 * g);
             float p[4], ds[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -214,7 +230,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
                 float pv = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, -l4[e]));
                 if constexpr (MASK) pv = kv > q0 + 32 * qh + qi + e ? 0.0f : pv;
                 p[e] = pv;
-                ds[e] = pv * (pacc[r] - d4[e]);
+                ds[e] = pv * pacc[r];
             }
             const int t = g >> 1;
             const int wd = (g & 1) * 2;
@@ -242,9 +258,17 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
     auto step = [&](int i, auto MASKC) {
         const int buf = (i - ib) & 1;
         if (i + 1 < nqb) issue(i + 1, buf ^ 1);
-        compute_half(buf, i * kQPerIter, std::integral_constant<int, 0>{}, MASKC);
+        compute_half(i * kQPerIter, std::integral_constant<int, 0>{}, MASKC);
         __builtin_amdgcn_sched_barrier(0);
-        compute_half(buf, i * kQPerIter, std::integral_constant<int, 1>{}, MASKC);
+        compute_half(i * kQPerIter, std::integral_constant<int, 1>{}, MASKC);
+        // the next iteration reads the other stage
+        qoff ^= QTILE;
+        ldoff ^= 2 * kQPerIter * 4;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            troff[db][0] ^= QTILE;
+            troff[db][1] ^= QTILE;
+        }
         wait_vmem();
         __syncthreads();
     };
@@ -312,7 +336,7 @@ __global__ __launch_bounds__(64 * kDqWaves<WIDE>, WIDE ? 1 : 2) void bwd_dq_kern
         of[ks] = buf_load16(rdO, off);
     }
     const float lse2 = buf_load4f(make_rsrc(L2vec + (size_t)bh * S, (uint32_t)S * 4), (uint32_t)qrow * 4);
-    const float dd = buf_load4f(make_rsrc(Dvec + (size_t)bh * S, (uint32_t)S * 4), (uint32_t)qrow * 4);
+    const float ndd = buf_load4f(make_rsrc(Dvec + (size_t)bh * S, (uint32_t)S * 4), (uint32_t)qrow * 4);  // -D
 
     fa_f32x16 dqacc[DB];
 #pragma unroll
@@ -370,7 +394,7 @@ __global__ __launch_bounds__(64 * kDqWaves<WIDE>, WIDE ? 1 : 2) void bwd_dq_kern
                         const bool dead = (CAUSAL && key > qrow) || key >= S;
                         pv = dead ? 0.0f : pv;
                     }
-                    ds[e] = pv * (pacc[mb][r + e] - dd);
+                    ds[e] = pv * (pacc[mb][r + e] + ndd);
                 }
                 dsf[2 * mb + (r >> 3)][(r & 7) >> 1] = pack_bf16(ds[0], ds[1]);
             }

@@ -30,8 +30,8 @@
  *     allocates nothing and keeps no state between calls.
  *   - Q, K, V, O, dO, dK, dV: bf16 (raw 16-bit patterns), contiguous
  *     row-major [B][H][S][d].  LSE: fp32 [B][H][S].  dQ: fp32 [B][H][S][d].
- *     The backward workspace holds D (fp32 [B][H][S]) followed by
- *     LSE * log2(e) (fp32 [B][H][S]).
+ *     The backward workspace holds -D (fp32 [B][H][S], D_i = sum_k dO_ik
+ *     O_ik, kept negated) followed by LSE * log2(e) (fp32 [B][H][S]).
  *   - Every pointer must be 16-byte aligned.
  *   - d must be 64 or 128.  S may be any value >= 0 (ragged tails are
  *     masked).  B, H >= 0.  B*H*S == 0 is a valid empty call that launches
@@ -98,7 +98,7 @@ fa_status fa_fwd_varlen(const void *Q, const void *K, const void *V, void *O, fl
                         const int *cu_seqlens, int nseq, int H, int total, int max_seqlen, int d,
                         float scale, int causal, void *stream);
 
-/* Bytes of workspace fa_bwd needs: 2*B*H*S fp32 values (D and LSE*log2 e). */
+/* Bytes of workspace fa_bwd needs: 2*B*H*S fp32 values (-D and LSE*log2 e). */
 size_t fa_bwd_workspace_bytes(int B, int H, int S, int d);
 
 /*
@@ -107,7 +107,7 @@ size_t fa_bwd_workspace_bytes(int B, int H, int S, int d);
  * (bf16 [B][H][S][d]); every element is written exactly once (no atomics),
  * so the result is bitwise reproducible.  workspace must hold at least
  * fa_bwd_workspace_bytes(B, H, S, d) bytes of device memory; its contents on
- * entry are ignored and on return are D and LSE*log2(e).  Outputs must not
+ * entry are ignored and on return are -D and LSE*log2(e).  Outputs must not
  * overlap inputs.
  * Equivalent to fa_bwd_preprocess, then fa_bwd_dkdv and fa_bwd_dq (the two
  * gradient kernels are independent of each other).
@@ -118,7 +118,7 @@ fa_status fa_bwd(const void *Q, const void *K, const void *V, const void *O, con
                  void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Step 1 of fa_bwd: D_i = sum_k dO_ik O_ik and LSE_i * log2(e), fp32, into
+ * Step 1 of fa_bwd: -D_i = -sum_k dO_ik O_ik and LSE_i * log2(e), fp32, into
  * workspace.  Same argument rules as fa_bwd.
  */
 fa_status fa_bwd_preprocess(const void *O, const void *dO, const float *LSE,
@@ -127,7 +127,7 @@ fa_status fa_bwd_preprocess(const void *O, const void *dO, const float *LSE,
 
 /*
  * Step 2 of fa_bwd: recompute P from LSE tile by tile and write dK and dV
- * (one workgroup per block of 128 keys).  Reads the D and LSE*log2(e) that
+ * (one workgroup per block of 256 keys).  Reads the -D and LSE*log2(e) that
  * fa_bwd_preprocess left in workspace on the same stream.
  */
 fa_status fa_bwd_dkdv(const void *Q, const void *K, const void *V,
@@ -136,8 +136,9 @@ fa_status fa_bwd_dkdv(const void *Q, const void *K, const void *V,
                       const void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Step 3 of fa_bwd: recompute P and dP per block of 128 queries and write
- * dQ = scale * dS K in fp32.  Reads the workspace like fa_bwd_dkdv.
+ * Step 3 of fa_bwd: recompute P and dP per block of 128 queries (256 for
+ * non-causal S >= 8192) and write dQ = scale * dS K in fp32.  Reads the
+ * workspace like fa_bwd_dkdv.
  */
 fa_status fa_bwd_dq(const void *Q, const void *K, const void *V,
                     const void *dO, float *dQ,

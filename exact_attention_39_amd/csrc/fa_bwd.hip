@@ -23,7 +23,8 @@
 // dK/dV kernel: one workgroup = 8 waves = 256 key rows; each wave owns 32
 // keys and takes the two 32-row halves of every 64-row query block in turn,
 // two waves per SIMD overlapping MFMA with softmax work.  V of the block
-// stays in LDS, each wave's K rows sit in registers (loaded once), dK and dV
+// stays in LDS (rows padded rather than swizzled, since V is only read by
+// rows), each wave's K rows sit in registers (loaded once), dK and dV
 // accumulate in registers; query blocks (Q, dO, LSE, D) stream through a
 // double-buffered LDS stage filled by direct memory-to-LDS copies, one
 // barrier per 64 queries x 256 keys.  Per wave and half block: S = Q K^T
@@ -109,7 +110,11 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
     constexpr int QTILE = kQPerIter * ROWB;
-    constexpr int VTILE = kKB * ROWB;
+    // V rows are padded by 16 bytes instead of swizzled: V is only read by
+    // rows, 16 consecutive rows at one chunk then start 4 banks apart, and
+    // the k-step becomes an immediate offset.
+    constexpr int VPITCH = ROWB + 16;
+    constexpr int VTILE = kKB * VPITCH;
     constexpr int LDB = 4 * kQPerIter * 4;
     constexpr int SMEM = LDB + 4 * QTILE + VTILE;
 
@@ -140,7 +145,23 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
     const fa_rsrc rL = make_rsrc(L2vec + (size_t)bh * S, (uint32_t)S * 4);
     const fa_rsrc rD = make_rsrc(Dvec + (size_t)bh * S, (uint32_t)S * 4);
 
-    tile_to_lds<NCH, kKB, NW>(make_rsrc(V + head, head_bytes), k0, sV, w, lane);
+    {
+        // V rows of the block into the padded tile, through registers (the
+        // memory-to-LDS copies write 1 KB contiguously)
+        const fa_rsrc rV = make_rsrc(V + head, head_bytes);
+        constexpr int CPT = kKB * NCH / (64 * NW);  // 16-byte chunks per thread
+        fa_u32x4 vt[CPT];
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            const int idx = (int)threadIdx.x + k * 64 * NW;
+            vt[k] = buf_load16(rV, (uint32_t)(k0 + idx / NCH) * ROWB + (idx % NCH) * 16);
+        }
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            const int idx = (int)threadIdx.x + k * 64 * NW;
+            lds_write16(sV, (idx / NCH) * VPITCH + (idx % NCH) * 16, vt[k]);
+        }
+    }
     // this wave's K rows, the B operands of S = Q K^T, straight to registers
     fa_u32x4 kreg[KS];
     {
@@ -173,14 +194,15 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
     __syncthreads();
 
     // Lane-dependent LDS offsets within query half 0 (half 1 is 32 rows,
-    // a multiple of the swizzle period, further on) and of this wave's V rows.
-    // The swizzle XORs the chunk index, so the offset of k-step ks is the
-    // offset of k-step 0 with 2 ks XORed into the chunk bits.  The query-side
-    // offsets (< QTILE / 2) carry the stage as bit QTILE, flipped after every
-    // iteration; the LSE/D offset carries it as bit 2 * kQPerIter * 4.
+    // a multiple of the swizzle period, further on) and of this wave's V rows
+    // (padded rows: k-step ks is 32 ks bytes further).  The swizzle XORs the
+    // chunk index, so the Q/dO offset of k-step ks is that of k-step 0 with
+    // 2 ks XORed into the chunk bits.  The query-side offsets (< QTILE / 2)
+    // carry the stage as bit QTILE, flipped after every iteration; the LSE/D
+    // offset carries it as bit 2 * kQPerIter * 4.
     int troff[DB][2];
     int qoff = tile_off<NCH>(n, h * 16);
-    const int voff0 = (int)(sV - smem) + tile_off<NCH>(32 * w + n, h * 16);
+    const int voff0 = (int)(sV - smem) + (32 * w + n) * VPITCH + h * 16;
     int ldoff = 16 * h;
     {
         const int L = lane & 15;
@@ -202,8 +224,8 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
 
         // fresh copies per half, so that the eight offsets are formed at
         // their reads rather than hoisted out of the loop into registers
-        int qb = qoff, vb = voff0;
-        asm volatile("" : "+v"(qb), "+v"(vb));
+        int qb = qoff;
+        asm volatile("" : "+v"(qb));
         // dP accumulates on top of -D of its query row, so it ends as dP - D
         fa_f32x16 sacc = zero16(), pacc;
 #pragma unroll
@@ -216,7 +238,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
         for (int ks = 0; ks < KS; ++ks) {
             const int qo = qb ^ (ks << 5);
             sacc = mfma32(lds_read16(sQ, qo), kreg[ks], sacc);
-            pacc = mfma32(lds_read16(sO, qo), lds_read16(smem, vb ^ (ks << 5)), pacc);
+            pacc = mfma32(lds_read16(sO, qo), lds_read16(smem, voff0 + 32 * ks), pacc);
         }
         fa_u32x4 pf[2], dsf[2];
 #pragma unroll

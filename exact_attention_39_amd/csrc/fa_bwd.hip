@@ -63,8 +63,8 @@ template <bool WIDE> constexpr int kKvPerTile = WIDE ? 128 : 64;
 
 // -D_i = -sum_k dO_ik O_ik and LSE_i * log2(e) (the base-2 exponent offset
 // the two gradient kernels use), both into the workspace.  D is kept negated
-// so that the dK/dV kernel can start its dP accumulators at -D and take
-// dS = P (dP - D) straight from them.
+// so that both gradient kernels can start their dP accumulators at -D and
+// take dS = P (dP - D) straight from them.
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const uint16_t *__restrict__ O,
                                                            const uint16_t *__restrict__ dO,
@@ -363,6 +363,11 @@ __global__ __launch_bounds__(64 * kDqWaves<WIDE>, WIDE ? 1 : 2) void bwd_dq_kern
     fa_f32x16 dqacc[DB];
 #pragma unroll
     for (int i = 0; i < DB; ++i) dqacc[i] = zero16();
+    // -D of this lane's query in every register: the dP^T accumulators
+    // start from it (the MFMA's C operand), so they end as dP - D
+    fa_f32x16 nd16;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) nd16[r] = ndd;
 
     auto issue_tile = [&](int j, int buf) {
         fa_lds_char *sK = smem + buf * 2 * TILE;
@@ -393,7 +398,7 @@ __global__ __launch_bounds__(64 * kDqWaves<WIDE>, WIDE ? 1 : 2) void bwd_dq_kern
         const fa_lds_char *sV = sK + TILE;
         // S^T = K Q^T and dP^T = V dO^T: 64 keys x 32 queries each.
         fa_f32x16 sacc[2] = {zero16(), zero16()};
-        fa_f32x16 pacc[2] = {zero16(), zero16()};
+        fa_f32x16 pacc[2] = {nd16, nd16};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
@@ -416,7 +421,7 @@ __global__ __launch_bounds__(64 * kDqWaves<WIDE>, WIDE ? 1 : 2) void bwd_dq_kern
                         const bool dead = (CAUSAL && key > qrow) || key >= S;
                         pv = dead ? 0.0f : pv;
                     }
-                    ds[e] = pv * (pacc[mb][r + e] + ndd);
+                    ds[e] = pv * pacc[mb][r + e];
                 }
                 dsf[2 * mb + (r >> 3)][(r & 7) >> 1] = pack_bf16(ds[0], ds[1]);
             }

@@ -13,6 +13,7 @@ events on the launch stream inside the timed region) and the CPU oracle
 timed on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --configs | --varlen | --ablation   (other measurements, see --help)
 """
 import argparse
 import hashlib
@@ -218,6 +219,67 @@ def varlen_bench(fa, gen, args, name="prefill_varlen_h16_d128"):
     }))
 
 
+def _events_ms(fn, warmup=3, reps=20):
+    """Per-call milliseconds of fn() (HIP events on the current stream around
+    each call) after `warmup` untimed calls: (median, min)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in evs:
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    t = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    return t[len(t) // 2], t[0]
+
+
+def configs_bench(fa, gen, args):
+    """Every workload of the suite, each direction it runs: 3 warm-up calls,
+    then 20 calls timed one by one; TFLOPS = counted FLOPs / median time.
+    One JSON line per (workload, mask, direction)."""
+    import numpy as np
+    import torch
+
+    def dev(b):
+        return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda()
+
+    for name, w in gen.WORKLOADS.items():
+        B, H, S, d = w["B"], w["H"], w["S"], w["d"]
+        scale = gen.default_scale(d)
+        print(f"[bench] configs: {name}", file=sys.stderr, flush=True)
+        tensors = ("q", "k", "v", "do") if w["bwd"] else ("q", "k", "v")
+        bits = gen.workload_inputs(name, tensors)
+        t = {k: dev(b) for k, b in bits.items()}
+        del bits
+        o = torch.empty_like(t["q"])
+        lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+        for causal in w["causal"]:
+            runs = [("fwd", lambda: fa.fa_fwd(t["q"], t["k"], t["v"], o, lse, scale, causal))]
+            if w["bwd"]:
+                fa.fa_fwd(t["q"], t["k"], t["v"], o, lse, scale, causal)
+                dq = torch.empty((B, H, S, d), dtype=torch.float32, device="cuda")
+                dk, dv = torch.empty_like(t["q"]), torch.empty_like(t["q"])
+                ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, S, d) // 4, dtype=torch.float32, device="cuda")
+                runs.append(("bwd", lambda: fa.fa_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], dq, dk, dv,
+                                                      scale, causal, ws)))
+            for direction, fn in runs:
+                med, mn = _events_ms(fn)
+                fl = flops(B, H, S, d, causal, direction == "bwd")
+                tf = fl / (med / 1e3) / 1e12
+                print(json.dumps({
+                    "metric": f"attention {direction} TFLOPS (median of 20 calls)", "value": round(tf, 1),
+                    "unit": "TFLOPS", "n_gpus": 1, "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+                    "ms_median": round(med, 4), "ms_min": round(mn, 4), "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+                    "config": {"workload": name, "B": B, "H": H, "S": S, "d": d, "causal": causal,
+                               "boost": w["boost"]},
+                }), flush=True)
+        del t, o, lse
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -228,6 +290,9 @@ def main():
     ap.add_argument("--varlen", action="store_true",
                     help="time the packed variable-length prefill forward (fa_fwd_varlen) on the "
                          "prefill_varlen_h16_d128 batch instead of the step; prints its own JSON line")
+    ap.add_argument("--configs", action="store_true",
+                    help="time every workload of the suite and direction it runs (3 warm-up calls, "
+                         "20 timed calls, median and minimum); one JSON line each, instead of the step")
     ap.add_argument("--ablation", action="store_true",
                     help="time the softmax options (hybrid exp share, polynomial degree, rescale "
                          "threshold) and the causal block order instead of the step")
@@ -248,6 +313,9 @@ def main():
     fa.fa_set_softmax_options(8.0, 0, 3)
     if args.varlen:
         varlen_bench(fa, gen, args)
+        return
+    if args.configs:
+        configs_bench(fa, gen, args)
         return
     w = gen.WORKLOADS[WORKLOAD]
     B, H, S, d = w["B"], w["H"], w["S"], w["d"]

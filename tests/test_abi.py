@@ -150,3 +150,14 @@ def test_varlen_binding_checks_shapes():
     cu = torch.tensor([0, 4, 10], dtype=torch.int32)
     with pytest.raises(ValueError, match="GPU"):
         fa.forward_varlen(q, q, q, cu, 6)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; --gpus N > 1 exits with a message, before
+    touching the GPU."""
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "not supported" in r.stderr and r.stdout == ""

@@ -307,6 +307,8 @@ def test_workload_forward_sampled(fa, name, causal):
 
 
 WORKLOAD_BWD = [
+    ("fwd_b4_h16_s4096", False),
+    ("causal_boost_b2_h16_s8192", True),  # every 64th query row x8: peaked rows
     ("causal_fwdbwd_b2_h16_s16384", True),
     ("long_b1_h16_s32768", False),
     ("long_b1_h16_s32768", True),

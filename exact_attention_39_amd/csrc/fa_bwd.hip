@@ -39,7 +39,9 @@
 // S^T = K Q^T, dP^T = V dO^T (queries on the lanes, so LSE and D are per
 // lane), dS^T in registers, dQ^T += K^T dS^T with K^T by transposing reads.
 //
-// scale is folded into dS once, so dK and dQ need no epilogue scaling.
+// In both kernels the dP accumulators start at -D (the workspace keeps D
+// negated), so they end as dP - D, and scale multiplies dK and dQ once in
+// the epilogues rather than every dS element.
 // Causal: key blocks only meet query blocks at or below the diagonal; both
 // kernels order workgroup ids so the longest blocks start first (LPT,
 // technical summary, results).

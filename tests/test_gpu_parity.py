@@ -339,13 +339,15 @@ def test_workload_backward_sampled(fa, name, causal):
     check_grad(bf16_to_np64(dv[b, h, cidx]), gv, f"{name} dV cols")
 
 
-@pytest.mark.parametrize("B,H,S,causal", [(2, 3, 3000, False), (2, 3, 3000, True), (1, 2, 8300, False)])
-def test_head_dim_64_sampled(fa, B, H, S, causal):
-    """d = 64 at multi-tile sizes with ragged tails: sampled forward rows, dQ
-    rows, dK/dV columns of two heads against the oracle.  Non-causal
-    S = 8300 takes the wide dQ shape (256 queries per workgroup)."""
-    d = 64
-    say(f"[d=64] B={B} H={H} S={S} causal={causal}")
+@pytest.mark.parametrize("B,H,S,d,causal", [(2, 3, 3000, 64, False), (2, 3, 3000, 64, True),
+                                             (1, 2, 8300, 64, False), (1, 2, 5000, 128, True),
+                                             (1, 2, 9000, 128, False)])
+def test_ragged_sampled(fa, B, H, S, d, causal):
+    """Multi-tile sizes with ragged tails (S not a multiple of 64 or 256),
+    both head dimensions: sampled forward rows, dQ rows, dK/dV columns of two
+    heads against the oracle.  Non-causal S >= 8192 takes the wide dQ shape
+    (256 queries per workgroup)."""
+    say(f"[ragged] B={B} H={H} S={S} d={d} causal={causal}")
     shape = (B, H, S, d)
     qb, kb, vb, dob = (rand_bits(shape, 7500 + i) for i in range(4))
     scale = 1.0 / np.sqrt(d)
@@ -358,13 +360,13 @@ def test_head_dim_64_sampled(fa, B, H, S, causal):
     for b, h in ((0, 0), (B - 1, H - 1)):
         Q, K, V, dO = (gen.bf16_bits_to_f64(x[b, h]) for x in (qb, kb, vb, dob))
         o_ref, l_ref = oracle.forward_rows(Q, K, V, rows, scale, causal)
-        check_o(bf16_to_np64(o[b, h, idx]), o_ref, f"d=64 O rows head ({b},{h})")
-        check_lse(lse[b, h, idx].cpu().numpy().astype(np.float64), l_ref, f"d=64 LSE rows head ({b},{h})")
+        check_o(bf16_to_np64(o[b, h, idx]), o_ref, f"d={d} O rows head ({b},{h})")
+        check_lse(lse[b, h, idx].cpu().numpy().astype(np.float64), l_ref, f"d={d} LSE rows head ({b},{h})")
         gq = oracle.backward_dq_rows(Q, K, V, dO, rows, scale, causal)
-        check_grad(dq[b, h, idx].cpu().numpy().astype(np.float64), gq, f"d=64 dQ rows head ({b},{h})")
+        check_grad(dq[b, h, idx].cpu().numpy().astype(np.float64), gq, f"d={d} dQ rows head ({b},{h})")
         gk, gv = oracle.backward_dkdv_cols(Q, K, V, dO, cols, scale, causal)
-        check_grad(bf16_to_np64(dk[b, h, cidx]), gk, f"d=64 dK cols head ({b},{h})")
-        check_grad(bf16_to_np64(dv[b, h, cidx]), gv, f"d=64 dV cols head ({b},{h})")
+        check_grad(bf16_to_np64(dk[b, h, cidx]), gk, f"d={d} dK cols head ({b},{h})")
+        check_grad(bf16_to_np64(dv[b, h, cidx]), gv, f"d={d} dV cols head ({b},{h})")
 
 
 def test_backward_is_bitwise_repeatable(fa):

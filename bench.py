@@ -84,8 +84,15 @@ def cpu_baseline(bits, S, d, scale, rows_n=2048):
     oracle.backward_dq_rows(Q, K, V, dO, rows, scale, False, nthreads=threads)
     dt = time.perf_counter() - t0
     counted = rows_n * (4.0 + 10.0) * S * d
+    cpu = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), cpu)
+    except OSError:
+        pass
     return {"value": counted / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
-            "sample": f"{rows_n} query rows of head 0, non-causal S={S} d={d}: oracle forward_rows + "
+            "sample": f"{rows_n} query rows of head 0, non-causal S={S} d={d} on {threads} threads of "
+                      f"{os.cpu_count()} ({cpu}): oracle forward_rows + "
                       f"backward_dq_rows, {dt:.1f} s; credited (4+10)*S*d FLOP per row like the GPU step "
                       f"(the dQ-rows routine does 8*S*d of the 10*S*d, so the CPU figure is flattered)"}
 

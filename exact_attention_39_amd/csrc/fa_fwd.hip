@@ -371,12 +371,21 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(
         };
 
         // Iteration j: S^T(j), then its softmax.
+        // The score waves issue their share of the copies after the S^T
+        // MFMAs, off the head of the critical path, and without a branch
+        // between S^T and the softmax (which would keep the compiler from
+        // interleaving them).  The copies past the last tile read rows at or
+        // past S (zeros) or rows no iteration uses, into slots no later
+        // iteration reads.
         auto iteration = [&](int j, auto MASKC, auto MAXFIRSTC) __attribute__((always_inline)) {
-            if (j + 1 < nkv) issue_k(j + 1);
-            if (j < nkv) issue_v(j);
             if (j < nkv) {
                 s_product(j);
+                issue_k(j + 1);
+                issue_v(j);
                 softmax(j, MASKC, MAXFIRSTC);
+            } else {
+                issue_k(j + 1);
+                issue_v(j);
             }
             wait_vmem();
             __syncthreads();

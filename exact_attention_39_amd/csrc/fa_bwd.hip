@@ -443,9 +443,11 @@ __global__ __launch_bounds__(64 * kDqWaves<WIDE>, WIDE ? 1 : 2) void bwd_dq_kern
 
     auto step = [&](int j, auto MASKC) {
         const int buf = j & 1;
-        if (j + 1 < nkv) issue_tile(j + 1, buf ^ 1);
 #pragma unroll
         for (int sub = 0; sub < KVT / 64; ++sub) {
+            // the next tile's copies go out after the first 64-key sub-tile
+            // of the wide shape (with one sub-tile: before it)
+            if (sub == KVT / 128 && j + 1 < nkv) issue_tile(j + 1, buf ^ 1);
             const int kv0 = j * KVT + 64 * sub;
             if constexpr (decltype(MASKC)::value) {
                 if (!(CAUSAL && kv0 > wq_lo + 31)) compute_tile(buf, kv0, sub, MASKC);

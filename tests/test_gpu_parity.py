@@ -167,9 +167,10 @@ def test_empty_inputs_launch_nothing(fa):
         assert o.shape == shape and lse.shape == shape[:3] and dq.shape == shape
 
 
-def test_forward_repeatable_and_rescale_options_agree(fa):
-    say("[ab] tau / poly options")
-    B, H, S, d = 1, 4, 1024, 128
+@pytest.mark.parametrize("d", [64, 128])
+def test_forward_repeatable_and_rescale_options_agree(fa, d):
+    say(f"[ab] tau / poly options d={d}")
+    B, H, S = 1, 4, 1024
     shape = (B, H, S, d)
     qb = rand_bits(shape, 77, scale=3.0)  # large scores: the running max moves often
     kb, vb = rand_bits(shape, 78), rand_bits(shape, 79)
@@ -425,6 +426,36 @@ def test_varlen_forward_matches_oracle_per_sequence(fa, lens, H, d, causal):
                                                   scale, causal)
         check_o(o_np[a:b].transpose(1, 0, 2), o_ref[0], f"varlen seq {s} (len {b - a})")
         check_lse(lse_np[:, a:b], lse_ref[0], f"varlen seq {s} (len {b - a})")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_varlen_softmax_options(fa, d):
+    """The packed forward under the other softmax options (max-first order,
+    hybrid exponentials) against the oracle, per sequence."""
+    lens, H = [300, 0, 131, 1, 77], 2
+    cu, total, qb, kb, vb = varlen_case(lens, H, d, 7300 + d)
+    scale = 1.0 / np.sqrt(d)
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    cu_d = torch.from_numpy(cu).cuda()
+    try:
+        for tau, poly, deg in [(0.0, 2, 5), (2.0, 1, 3)]:
+            fa.fa_set_softmax_options(tau, poly, deg)
+            for causal in (False, True):
+                say(f"[varlen options] d={d} tau={tau} poly={poly}/8 deg={deg} causal={causal}")
+                o, lse = fa.forward_varlen(q, k, v, cu_d, max(lens), causal=causal, scale=scale)
+                torch.cuda.synchronize()
+                o_np, lse_np = bf16_to_np64(o), lse.cpu().numpy().astype(np.float64)
+                for sq in range(len(lens)):
+                    a, b = int(cu[sq]), int(cu[sq + 1])
+                    if a == b:
+                        continue
+                    o_ref, lse_ref = oracle.attention_forward(seq_f64(qb, a, b), seq_f64(kb, a, b),
+                                                              seq_f64(vb, a, b), scale, causal)
+                    what = f"varlen seq {sq} tau={tau} poly={poly} deg={deg} causal={causal}"
+                    check_o(o_np[a:b].transpose(1, 0, 2), o_ref[0], what)
+                    check_lse(lse_np[:, a:b], lse_ref[0], what)
+    finally:
+        fa.fa_set_softmax_options(8.0, 0, 3)
 
 
 def test_varlen_equals_dense_forward_bitwise(fa):

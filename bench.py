@@ -112,13 +112,12 @@ def _time(fn, reps=5):
 
 
 def _sweep(configs, rounds=3):
-    """Median launch time of each (key, set_options, launch) in configs, the
+    """Median launch time of each (key, launch) in configs, the
     configurations interleaved over `rounds` rounds so that clock and
     warm-up drift do not favour any of them."""
     times = {}
     for _ in range(rounds):
-        for key, setup, fn in configs:
-            setup()
+        for key, fn in configs:
             times.setdefault(key, []).append(_time(fn))
     return {k: sorted(v)[len(v) // 2] for k, v in times.items()}
 
@@ -136,8 +135,8 @@ def ablation(fa, gen, dev, q, k, v, do, B, H, S, d, scale):
     opts = [(8.0, 0, 3), (0.0, 0, 3), (8.0, 1, 3), (8.0, 2, 3), (8.0, 1, 5), (8.0, 2, 5)]
 
     def option_rows(wname, qq, kk, vv, oo, ll, sc, shape, options, causals):
-        cfgs = [((opt, causal), (lambda opt=opt: fa.fa_set_softmax_options(*opt)),
-                 (lambda causal=causal: fa.fa_fwd(qq, kk, vv, oo, ll, sc, causal)))
+        cfgs = [((opt, causal),
+                 (lambda causal=causal, opt=opt: fa.fa_fwd(qq, kk, vv, oo, ll, sc, causal, opts=fa.Options(*opt))))
                 for opt in options for causal in causals]
         med = _sweep(cfgs)
         for (opt, causal), ms in med.items():
@@ -145,7 +144,6 @@ def ablation(fa, gen, dev, q, k, v, do, B, H, S, d, scale):
             rows.append({"kernel": "fwd", "workload": wname, "causal": causal, "tau": opt[0],
                          "poly_eighths": opt[1], "poly_degree": opt[2], "ms": round(ms, 4),
                          "tflops": round(fl / ms / 1e9, 1)})
-        fa.fa_set_softmax_options(8.0, 0, 3)
 
     option_rows(WORKLOAD, q, k, v, o, lse, scale, (B, H, S, d), opts, (False, True))
     # the same options at a shorter sequence (B = 4, H = 16, S = 4096), and
@@ -164,19 +162,18 @@ def ablation(fa, gen, dev, q, k, v, do, B, H, S, d, scale):
     # causal block order: longest first (LPT) vs shortest first
     fa.fa_fwd(q, k, v, o, lse, scale, True)
     fa.fa_bwd_preprocess(o, do, lse, ws)
-    kernels = (("fwd", lambda: fa.fa_fwd(q, k, v, o, lse, scale, True), flops(B, H, S, d, True, False)),
-               ("bwd_dkdv", lambda: fa.fa_bwd_dkdv(q, k, v, do, dk, dv, scale, True, ws),
+    kernels = (("fwd", lambda op: fa.fa_fwd(q, k, v, o, lse, scale, True, opts=op), flops(B, H, S, d, True, False)),
+               ("bwd_dkdv", lambda op: fa.fa_bwd_dkdv(q, k, v, do, dk, dv, scale, True, ws, opts=op),
                 0.8 * flops(B, H, S, d, True, True)),
-               ("bwd_dq", lambda: fa.fa_bwd_dq(q, k, v, do, dq, scale, True, ws),
+               ("bwd_dq", lambda op: fa.fa_bwd_dq(q, k, v, do, dq, scale, True, ws, opts=op),
                 0.2 * flops(B, H, S, d, True, True)))
-    cfgs = [((name, lpt), (lambda lpt=lpt: fa.fa_set_causal_order(lpt)), fn)
+    cfgs = [((name, lpt), (lambda fn=fn, lpt=lpt: fn(fa.Options(longest_first=lpt))))
             for lpt in (True, False) for name, fn, _ in kernels]
     med = _sweep(cfgs)
     fl_of = {name: fl for name, _, fl in kernels}
     for (name, lpt), ms in med.items():
         rows.append({"kernel": name, "workload": WORKLOAD, "causal": True, "longest_first": lpt,
                      "ms": round(ms, 4), "tflops": round(fl_of[name] / ms / 1e9, 1)})
-    fa.fa_set_causal_order(True)
     print(json.dumps({"ablation": rows}), flush=True)
 
 
@@ -224,6 +221,51 @@ def varlen_bench(fa, gen, args, name="prefill_varlen_h16_d128"):
         "config": {"workload": name, "nseq": int(len(lens)), "total_tokens": total, "H": H, "d": d,
                    "min_len": int(lens.min()), "max_len": maxlen, "causal": w["causal"]},
     }))
+
+
+GEMM_N = 16384
+
+
+def gemm_ceiling(args):
+    """The practical MFMA ceiling on this GPU: the library bf16 GEMM
+    (torch.matmul -> hipBLASLt), n = 16384, on N(0,1) operands (the data the
+    attention workloads feed their MFMAs) and on constant operands (all ones,
+    which toggle no datapath bits and so draw less power).  3 warm-up calls,
+    then 10 calls timed one by one with HIP events; TFLOPS = 2 n^3 / median.
+    One JSON line per operand kind."""
+    import torch
+    n = GEMM_N
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0xFA)
+    for kind in ("normal", "ones"):
+        if kind == "normal":
+            a = torch.randn((n, n), device="cuda", generator=g).to(torch.bfloat16)
+            b = torch.randn((n, n), device="cuda", generator=g).to(torch.bfloat16)
+        else:
+            a = torch.ones((n, n), device="cuda", dtype=torch.bfloat16)
+            b = torch.ones((n, n), device="cuda", dtype=torch.bfloat16)
+        c = torch.empty((n, n), device="cuda", dtype=torch.bfloat16)
+        med, mn = _events_ms(lambda: torch.matmul(a, b, out=c), warmup=3, reps=10)
+        tf = 2.0 * n ** 3 / (med / 1e3) / 1e12
+        print(json.dumps({"metric": "library bf16 GEMM TFLOPS (median of 10 calls)", "operands": kind, "n": n,
+                          "value": round(tf, 1), "unit": "TFLOPS", "ms_median": round(med, 4),
+                          "ms_min": round(mn, 4), "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}), flush=True)
+        del a, b, c
+        torch.cuda.empty_cache()
+
+
+def gemm_ceiling_tflops():
+    """The N(0,1) GEMM rate recorded in profiles/gemm_ceiling.txt (line
+    `ceiling_tflops_normal V`), or None."""
+    try:
+        with open(os.path.join(TRAFFIC_DIR, "gemm_ceiling.txt")) as f:
+            for line in f:
+                parts = line.split()
+                if len(parts) == 2 and parts[0] == "ceiling_tflops_normal":
+                    return float(parts[1])
+    except (OSError, ValueError):
+        pass
+    return None
 
 
 def _events_ms(fn, warmup=3, reps=20):
@@ -303,6 +345,9 @@ def main():
     ap.add_argument("--ablation", action="store_true",
                     help="time the softmax options (hybrid exp share, polynomial degree, rescale "
                          "threshold) and the causal block order instead of the step")
+    ap.add_argument("--gemm-ceiling", action="store_true",
+                    help="time the library bf16 GEMM (n = 16384) on N(0,1) and on constant operands: "
+                         "the practical MFMA ceiling the attention kernels are compared with")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: this build measures one MI355X "
@@ -317,7 +362,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     fa.load_library()
-    fa.fa_set_softmax_options(8.0, 0, 3)
+    if args.gemm_ceiling:
+        gemm_ceiling(args)
+        return
     if args.varlen:
         varlen_bench(fa, gen, args)
         return
@@ -418,6 +465,10 @@ def main():
         roof = {"bound": "mfma", "achieved": alg / (part_ms[dom] / 1e3) / 1e12, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    if roof["unit"] == "TFLOP/s":
+        # the library GEMM's rate on N(0,1) operands (profiles/gemm_ceiling.txt): what the same MFMAs
+        # reach on this GPU under its power limit; frac stays against the published peak
+        roof["ceiling"] = gemm_ceiling_tflops()
     roof["achieved"] = round(roof["achieved"], 1)
     roof["frac"] = round(roof["frac"], 4)
     roof["kernel"] = f"{kname}<d=128,causal={int(causal)}>"

@@ -6,7 +6,10 @@ the current HIP stream.  There is no fallback: if libfa.so is missing or the
 tensors are not on the GPU, the calls raise.
 
 Low-level functions carry the C names (``fa_fwd``, ``fa_bwd``, ...) and take
-torch tensors; ``forward`` / ``backward`` allocate their outputs.
+torch tensors; ``forward`` / ``backward`` allocate their outputs (on the
+stream they launch on, so that the caching allocator does not hand their
+memory to other work while the kernels still use it).  Tuning options go
+with each call as an ``Options`` value (None = the library defaults).
 """
 from __future__ import annotations
 
@@ -19,6 +22,20 @@ LIB_PATH = os.path.join(PKG, "libfa.so")
 FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 
 _lib = None
+
+
+class Options(ctypes.Structure):
+    """Per-call tuning options (struct fa_options of include/fa.h)."""
+    _fields_ = [("rescale_tau", ctypes.c_float), ("poly_eighths", ctypes.c_int),
+                ("poly_degree", ctypes.c_int), ("longest_first", ctypes.c_int)]
+
+    def __init__(self, rescale_tau: float = 8.0, poly_eighths: int = 0, poly_degree: int = 3,
+                 longest_first: bool = True):
+        super().__init__(float(rescale_tau), int(poly_eighths), int(poly_degree), int(bool(longest_first)))
+
+    def __repr__(self):
+        return (f"Options(rescale_tau={self.rescale_tau}, poly_eighths={self.poly_eighths}, "
+                f"poly_degree={self.poly_degree}, longest_first={bool(self.longest_first)})")
 
 
 class FaError(RuntimeError):
@@ -39,24 +56,27 @@ def load_library():
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
+    op = ctypes.POINTER(Options)
+    lib.fa_default_options.argtypes = []
+    lib.fa_default_options.restype = Options
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
     lib.fa_fwd.restype = i
-    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd_opt.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, op, vp]
+    lib.fa_fwd_opt.restype = i
+    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, op, vp]
     lib.fa_fwd_varlen.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_bwd.restype = i
+    lib.fa_bwd_opt.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, op, vp, sz, vp]
+    lib.fa_bwd_opt.restype = i
     lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, vp, sz, vp]
     lib.fa_bwd_preprocess.restype = i
-    lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, op, vp, sz, vp]
     lib.fa_bwd_dkdv.restype = i
-    lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, op, vp, sz, vp]
     lib.fa_bwd_dq.restype = i
-    lib.fa_set_softmax_options.argtypes = [f, i, i]
-    lib.fa_set_softmax_options.restype = i
-    lib.fa_set_causal_order.argtypes = [i]
-    lib.fa_set_causal_order.restype = i
     lib.fa_exp2_poly.argtypes = [vp, vp, ctypes.c_int64, i, vp]
     lib.fa_exp2_poly.restype = i
     _lib = lib
@@ -82,6 +102,19 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _opts(opts):
+    """Options -> pointer argument (None -> NULL, the library defaults)."""
+    if opts is None:
+        return None
+    if not isinstance(opts, Options):
+        raise TypeError("opts must be an exact_attention_39_amd.Options or None")
+    return ctypes.byref(opts)
+
+
+def default_options() -> Options:
+    return load_library().fa_default_options()
+
+
 def _check_tensor(t, name, dtype, shape):
     import torch
     if not isinstance(t, torch.Tensor):
@@ -103,17 +136,19 @@ def _dims(q):
 
 
 # ------------------------------------------------------------------ C names
-def fa_fwd(q, k, v, o, lse, scale: float, causal: bool, stream=None):
+def fa_fwd(q, k, v, o, lse, scale: float, causal: bool, stream=None, opts=None):
     import torch
     B, H, S, d = _dims(q)
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
         _check_tensor(t, nm, torch.bfloat16, (B, H, S, d))
     _check_tensor(lse, "lse", torch.float32, (B, H, S))
-    _check(load_library().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, S, d,
-                                 float(scale), int(bool(causal)), _stream(stream)), "fa_fwd")
+    _check(load_library().fa_fwd_opt(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, S, d,
+                                     float(scale), int(bool(causal)), _opts(opts), _stream(stream)),
+           "fa_fwd")
 
 
-def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, max_seqlen: int, scale: float, causal: bool, stream=None):
+def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, max_seqlen: int, scale: float, causal: bool, stream=None,
+                  opts=None):
     """Packed variable-length forward: q, k, v, o bf16 [total, H, d]; lse fp32
     [H, total]; cu_seqlens int32 [nseq + 1] on the GPU."""
     import torch
@@ -129,7 +164,7 @@ def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, max_seqlen: int, scale: float, ca
     nseq = cu_seqlens.numel() - 1
     _check(load_library().fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens),
                                         nseq, H, total, int(max_seqlen), d, float(scale),
-                                        int(bool(causal)), _stream(stream)), "fa_fwd_varlen")
+                                        int(bool(causal)), _opts(opts), _stream(stream)), "fa_fwd_varlen")
 
 
 def fa_bwd_workspace_bytes(B: int, H: int, S: int, d: int) -> int:
@@ -148,12 +183,12 @@ def _bwd_checks(q, k, v, o, lse, do, dq, dk, dv):
     return B, H, S, d
 
 
-def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, scale: float, causal: bool, workspace, stream=None):
+def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, scale: float, causal: bool, workspace, stream=None, opts=None):
     B, H, S, d = _bwd_checks(q, k, v, o, lse, do, dq, dk, dv)
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check(load_library().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
-                                 _ptr(dk), _ptr(dv), B, H, S, d, float(scale), int(bool(causal)),
-                                 _ptr(workspace), ws_bytes, _stream(stream)), "fa_bwd")
+    _check(load_library().fa_bwd_opt(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
+                                     _ptr(dk), _ptr(dv), B, H, S, d, float(scale), int(bool(causal)),
+                                     _opts(opts), _ptr(workspace), ws_bytes, _stream(stream)), "fa_bwd")
 
 
 def fa_bwd_preprocess(o, do, lse, workspace, stream=None):
@@ -175,7 +210,7 @@ def _grad_checks(q, k, v, do):
     return B, H, S, d
 
 
-def fa_bwd_dkdv(q, k, v, do, dk, dv, scale: float, causal: bool, workspace, stream=None):
+def fa_bwd_dkdv(q, k, v, do, dk, dv, scale: float, causal: bool, workspace, stream=None, opts=None):
     """dK, dV from the workspace that fa_bwd_preprocess filled on the same stream."""
     import torch
     B, H, S, d = _grad_checks(q, k, v, do)
@@ -183,28 +218,19 @@ def fa_bwd_dkdv(q, k, v, do, dk, dv, scale: float, causal: bool, workspace, stre
     _check_tensor(dv, "dv", torch.bfloat16, (B, H, S, d))
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(load_library().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dk), _ptr(dv),
-                                      B, H, S, d, float(scale), int(bool(causal)), _ptr(workspace), ws_bytes,
-                                      _stream(stream)), "fa_bwd_dkdv")
+                                      B, H, S, d, float(scale), int(bool(causal)), _opts(opts), _ptr(workspace),
+                                      ws_bytes, _stream(stream)), "fa_bwd_dkdv")
 
 
-def fa_bwd_dq(q, k, v, do, dq, scale: float, causal: bool, workspace, stream=None):
+def fa_bwd_dq(q, k, v, do, dq, scale: float, causal: bool, workspace, stream=None, opts=None):
     """dQ from the workspace that fa_bwd_preprocess filled on the same stream."""
     import torch
     B, H, S, d = _grad_checks(q, k, v, do)
     _check_tensor(dq, "dq", torch.float32, (B, H, S, d))
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(load_library().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), B, H, S, d,
-                                    float(scale), int(bool(causal)), _ptr(workspace), ws_bytes,
+                                    float(scale), int(bool(causal)), _opts(opts), _ptr(workspace), ws_bytes,
                                     _stream(stream)), "fa_bwd_dq")
-
-
-def fa_set_softmax_options(rescale_tau: float = 8.0, poly_eighths: int = 0, poly_degree: int = 3):
-    _check(load_library().fa_set_softmax_options(float(rescale_tau), int(poly_eighths), int(poly_degree)),
-           "fa_set_softmax_options")
-
-
-def fa_set_causal_order(longest_first: bool = True):
-    _check(load_library().fa_set_causal_order(int(bool(longest_first))), "fa_set_causal_order")
 
 
 def fa_exp2_poly(x, y, degree: int = 3, stream=None):
@@ -216,38 +242,59 @@ def fa_exp2_poly(x, y, degree: int = 3, stream=None):
 
 
 # ------------------------------------------------------------------ allocating wrappers
-def forward(q, k, v, causal: bool = False, scale: float | None = None, stream=None):
-    """(O bf16 [B,H,S,d], LSE fp32 [B,H,S]) for bf16 q, k, v on the GPU."""
+def _launch_stream(stream, *tensors):
+    """The stream the kernels go on; the tensors are checked to be on the GPU
+    first, so that a CPU tensor gets the clear error rather than a stream
+    lookup failure."""
+    import torch
+    for t in tensors:
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError("inputs must be torch tensors on the GPU (the attention path has no CPU fallback)")
+    return torch.cuda.current_stream() if stream is None else stream
+
+
+def forward(q, k, v, causal: bool = False, scale: float | None = None, stream=None, opts=None):
+    """(O bf16 [B,H,S,d], LSE fp32 [B,H,S]) for bf16 q, k, v on the GPU.
+    The outputs are allocated on the launch stream."""
     import torch
     B, H, S, d = _dims(q)
     scale = d ** -0.5 if scale is None else scale
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
-    fa_fwd(q, k, v, o, lse, scale, causal, stream)
+    s = _launch_stream(stream, q, k, v)
+    with torch.cuda.stream(s):
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    fa_fwd(q, k, v, o, lse, scale, causal, s, opts)
     return o, lse
 
 
 def forward_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False, scale: float | None = None,
-                   stream=None):
+                   stream=None, opts=None):
     """(O bf16 [total, H, d], LSE fp32 [H, total]) for a packed batch of
     sequences delimited by cu_seqlens (int32 [nseq + 1] on the GPU)."""
     import torch
     total, H, d = (int(x) for x in q.shape)
     scale = d ** -0.5 if scale is None else scale
-    o = torch.empty_like(q)
-    lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
-    fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, max_seqlen, scale, causal, stream)
+    s = _launch_stream(stream, q, k, v, cu_seqlens)
+    with torch.cuda.stream(s):
+        o = torch.empty_like(q)
+        lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, max_seqlen, scale, causal, s, opts)
     return o, lse
 
 
-def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, stream=None):
-    """(dQ fp32, dK bf16, dV bf16) for the O, LSE that ``forward`` returned."""
+def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, stream=None, opts=None):
+    """(dQ fp32, dK bf16, dV bf16) for the O, LSE that ``forward`` returned.
+    Outputs and the workspace are allocated on the launch stream: the
+    workspace returns to that stream's pool when this function returns, so
+    later allocations on it are ordered after the kernels that read it."""
     import torch
     B, H, S, d = _dims(q)
     scale = d ** -0.5 if scale is None else scale
-    dq = torch.empty((B, H, S, d), dtype=torch.float32, device=q.device)
-    dk = torch.empty_like(q)
-    dv = torch.empty_like(q)
-    ws = torch.empty(max(1, fa_bwd_workspace_bytes(B, H, S, d) // 4), dtype=torch.float32, device=q.device)
-    fa_bwd(q, k, v, o, lse, do, dq, dk, dv, scale, causal, ws, stream)
+    s = _launch_stream(stream, q, k, v, o, lse, do)
+    with torch.cuda.stream(s):
+        dq = torch.empty((B, H, S, d), dtype=torch.float32, device=q.device)
+        dk = torch.empty_like(q)
+        dv = torch.empty_like(q)
+        ws = torch.empty(max(1, fa_bwd_workspace_bytes(B, H, S, d) // 4), dtype=torch.float32, device=q.device)
+    fa_bwd(q, k, v, o, lse, do, dq, dk, dv, scale, causal, ws, s, opts)
     return dq, dk, dv

@@ -1,10 +1,11 @@
-// fa_api.hip -- the C ABI declared in include/fa.h: argument validation,
-// template dispatch and the softmax tuning knobs.  No allocation, no
-// synchronisation; every launch goes on the caller's stream.
+// fa_api.hip -- the C ABI declared in include/fa.h: argument validation and
+// template dispatch.  No allocation, no synchronisation, no mutable state:
+// the tuning options arrive with each call and are copied once on entry;
+// every launch goes on the caller's stream.
 #include <math.h>
 #include <stdint.h>
 
-#include <atomic>
+#include <algorithm>
 
 #include "exp2_poly.h"
 #include "fa.h"
@@ -13,10 +14,20 @@
 
 namespace {
 
-std::atomic<float> g_tau{8.0f};
-std::atomic<int> g_poly_eighths{0};
-std::atomic<int> g_poly_degree{3};
-std::atomic<int> g_lpt{1};
+constexpr fa_options kDefaultOptions = {8.0f, 0, 3, 1};
+
+// Copies the caller's options (NULL = defaults) into *out once, so the
+// launches of one call all see the same values; false if a field is out of
+// range.
+bool read_options(const fa_options *opts, fa_options *out) {
+    const fa_options o = opts ? *opts : kDefaultOptions;
+    if (!isfinite(o.rescale_tau) || o.rescale_tau < 0.0f || o.rescale_tau > 64.0f) return false;
+    if (o.poly_eighths < 0 || o.poly_eighths > 2) return false;
+    if (o.poly_degree != 3 && o.poly_degree != 5) return false;
+    if (o.longest_first != 0 && o.longest_first != 1) return false;
+    *out = o;
+    return true;
+}
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -66,24 +77,12 @@ const char *fa_status_string(fa_status s) {
     return "unknown fa_status";
 }
 
-fa_status fa_set_softmax_options(float rescale_tau, int poly_eighths, int poly_degree) {
-    if (!isfinite(rescale_tau) || rescale_tau < 0.0f || rescale_tau > 64.0f) return FA_ERR_INVALID;
-    if (poly_eighths < 0 || poly_eighths > 2) return FA_ERR_INVALID;
-    if (poly_degree != 3 && poly_degree != 5) return FA_ERR_INVALID;
-    g_tau.store(rescale_tau);
-    g_poly_eighths.store(poly_eighths);
-    g_poly_degree.store(poly_degree);
-    return FA_OK;
-}
+fa_options fa_default_options(void) { return kDefaultOptions; }
 
-fa_status fa_set_causal_order(int longest_first) {
-    if (longest_first != 0 && longest_first != 1) return FA_ERR_INVALID;
-    g_lpt.store(longest_first);
-    return FA_OK;
-}
-
-fa_status fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE, int B, int H,
-                 int S, int d, float scale, int causal, void *stream) {
+fa_status fa_fwd_opt(const void *Q, const void *K, const void *V, void *O, float *LSE, int B, int H,
+                     int S, int d, float scale, int causal, const fa_options *opts, void *stream) {
+    fa_options o;
+    if (!read_options(opts, &o)) return FA_ERR_INVALID;
     bool empty = false;
     fa_status st = check_shape(B, H, S, d, &empty);
     if (st != FA_OK) return st;
@@ -93,19 +92,31 @@ fa_status fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LS
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
         return FA_ERR_INVALID;
     fa::FwdArgs a{Q, K, V, O, LSE, B * H, S, d, scale, causal == 1,
-                  g_tau.load(), g_poly_eighths.load(), g_poly_degree.load(), g_lpt.load() != 0};
+                  o.rescale_tau, o.poly_eighths, o.poly_degree, o.longest_first != 0};
     return hip_status(fa::launch_fwd(a, (hipStream_t)stream));
+}
+
+fa_status fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE, int B, int H,
+                 int S, int d, float scale, int causal, void *stream) {
+    return fa_fwd_opt(Q, K, V, O, LSE, B, H, S, d, scale, causal, nullptr, stream);
 }
 
 fa_status fa_fwd_varlen(const void *Q, const void *K, const void *V, void *O, float *LSE,
                         const int *cu_seqlens, int nseq, int H, int total, int max_seqlen, int d,
-                        float scale, int causal, void *stream) {
+                        float scale, int causal, const fa_options *opts, void *stream) {
+    fa_options o;
+    if (!read_options(opts, &o)) return FA_ERR_INVALID;
     if (nseq < 0 || H < 0 || total < 0 || max_seqlen < 0) return FA_ERR_INVALID;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (!good_scale(scale) || (causal != 0 && causal != 1)) return FA_ERR_INVALID;
     if (max_seqlen > (1 << 22)) return FA_ERR_INVALID;
-    // byte offsets inside one (sequence, head) stay 32-bit: total * H * d * 2 < 2^32
-    if ((int64_t)total * H * d * 2 >= ((int64_t)1 << 32)) return FA_ERR_INVALID;
+    // Byte offsets inside one (sequence, head) are 32-bit.  The kernel
+    // addresses query/output rows up to max_seqlen rounded up to its 256-row
+    // blocks, and key/value rows up to 191 past the end of a sequence (tile
+    // copies of the next iteration), at a pitch of H * d * 2 bytes: every such
+    // offset must stay below 2^32, or it would wrap onto valid rows.
+    const int64_t reach = std::max(((int64_t)max_seqlen + 255) / 256 * 256, (int64_t)total + 192);
+    if (reach * H * d * 2 > ((int64_t)1 << 32)) return FA_ERR_INVALID;
     const int64_t units = (int64_t)nseq * H;
     if (units > INT32_MAX || units * (((int64_t)max_seqlen + 63) / 64) > INT32_MAX) return FA_ERR_INVALID;
     if (units == 0 || total == 0 || max_seqlen == 0) return FA_OK;
@@ -114,7 +125,7 @@ fa_status fa_fwd_varlen(const void *Q, const void *K, const void *V, void *O, fl
         ((uintptr_t)cu_seqlens & 3u) != 0)
         return FA_ERR_INVALID;
     fa::FwdArgs a{Q, K, V, O, LSE, (int)units, max_seqlen, d, scale, causal == 1,
-                  g_tau.load(), g_poly_eighths.load(), g_poly_degree.load(), g_lpt.load() != 0};
+                  o.rescale_tau, o.poly_eighths, o.poly_degree, o.longest_first != 0};
     a.cu_seqlens = cu_seqlens;
     a.H = H;
     a.total = total;
@@ -157,8 +168,10 @@ fa_status fa_bwd_preprocess(const void *O, const void *dO, const float *LSE, int
 // Common checks of the two gradient kernels; fills the launch arguments.
 static fa_status bwd_grad_args(const void *Q, const void *K, const void *V,
                                const void *dO, int B, int H, int S, int d, float scale, int causal,
-                               const void *workspace, size_t workspace_bytes, fa::BwdArgs *a,
-                               bool *empty) {
+                               const fa_options *opts, const void *workspace, size_t workspace_bytes,
+                               fa::BwdArgs *a, bool *empty) {
+    fa_options o;
+    if (!read_options(opts, &o)) return FA_ERR_INVALID;
     fa_status st = check_bwd_common(B, H, S, d, workspace, workspace_bytes, empty);
     if (st != FA_OK) return st;
     if (!good_scale(scale) || (causal != 0 && causal != 1)) return FA_ERR_INVALID;
@@ -177,16 +190,17 @@ static fa_status bwd_grad_args(const void *Q, const void *K, const void *V,
     a->d = d;
     a->scale = scale;
     a->causal = causal == 1;
-    a->lpt = g_lpt.load() != 0;
+    a->lpt = o.longest_first != 0;
     return FA_OK;
 }
 
 fa_status fa_bwd_dkdv(const void *Q, const void *K, const void *V, const void *dO,
                       void *dK, void *dV, int B, int H, int S, int d, float scale, int causal,
-                      const void *workspace, size_t workspace_bytes, void *stream) {
+                      const fa_options *opts, const void *workspace, size_t workspace_bytes,
+                      void *stream) {
     fa::BwdArgs a;
     bool empty = false;
-    fa_status st = bwd_grad_args(Q, K, V, dO, B, H, S, d, scale, causal, workspace,
+    fa_status st = bwd_grad_args(Q, K, V, dO, B, H, S, d, scale, causal, opts, workspace,
                                  workspace_bytes, &a, &empty);
     if (st != FA_OK || empty) return st;
     if (!dK || !dV || !aligned16(dK) || !aligned16(dV)) return FA_ERR_INVALID;
@@ -197,10 +211,11 @@ fa_status fa_bwd_dkdv(const void *Q, const void *K, const void *V, const void *d
 
 fa_status fa_bwd_dq(const void *Q, const void *K, const void *V, const void *dO,
                     float *dQ, int B, int H, int S, int d, float scale, int causal,
-                    const void *workspace, size_t workspace_bytes, void *stream) {
+                    const fa_options *opts, const void *workspace, size_t workspace_bytes,
+                    void *stream) {
     fa::BwdArgs a;
     bool empty = false;
-    fa_status st = bwd_grad_args(Q, K, V, dO, B, H, S, d, scale, causal, workspace,
+    fa_status st = bwd_grad_args(Q, K, V, dO, B, H, S, d, scale, causal, opts, workspace,
                                  workspace_bytes, &a, &empty);
     if (st != FA_OK || empty) return st;
     if (!dQ || !aligned16(dQ)) return FA_ERR_INVALID;
@@ -208,12 +223,15 @@ fa_status fa_bwd_dq(const void *Q, const void *K, const void *V, const void *dO,
     return hip_status(fa::launch_bwd_dq(a, (hipStream_t)stream));
 }
 
-fa_status fa_bwd(const void *Q, const void *K, const void *V, const void *O, const float *LSE,
-                 const void *dO, float *dQ, void *dK, void *dV, int B, int H, int S, int d,
-                 float scale, int causal, void *workspace, size_t workspace_bytes, void *stream) {
+fa_status fa_bwd_opt(const void *Q, const void *K, const void *V, const void *O, const float *LSE,
+                     const void *dO, float *dQ, void *dK, void *dV, int B, int H, int S, int d,
+                     float scale, int causal, const fa_options *opts, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+    fa_options o;
+    if (!read_options(opts, &o)) return FA_ERR_INVALID;
     fa::BwdArgs a;
     bool empty = false;
-    fa_status st = bwd_grad_args(Q, K, V, dO, B, H, S, d, scale, causal, workspace,
+    fa_status st = bwd_grad_args(Q, K, V, dO, B, H, S, d, scale, causal, &o, workspace,
                                  workspace_bytes, &a, &empty);
     if (st != FA_OK || empty) return st;
     const void *outs[] = {O, LSE, dQ, dK, dV};
@@ -221,9 +239,17 @@ fa_status fa_bwd(const void *Q, const void *K, const void *V, const void *O, con
         if (!p || !aligned16(p)) return FA_ERR_INVALID;
     st = fa_bwd_preprocess(O, dO, LSE, B, H, S, d, workspace, workspace_bytes, stream);
     if (st != FA_OK) return st;
-    st = fa_bwd_dkdv(Q, K, V, dO, dK, dV, B, H, S, d, scale, causal, workspace, workspace_bytes, stream);
+    st = fa_bwd_dkdv(Q, K, V, dO, dK, dV, B, H, S, d, scale, causal, &o, workspace, workspace_bytes,
+                     stream);
     if (st != FA_OK) return st;
-    return fa_bwd_dq(Q, K, V, dO, dQ, B, H, S, d, scale, causal, workspace, workspace_bytes, stream);
+    return fa_bwd_dq(Q, K, V, dO, dQ, B, H, S, d, scale, causal, &o, workspace, workspace_bytes, stream);
+}
+
+fa_status fa_bwd(const void *Q, const void *K, const void *V, const void *O, const float *LSE,
+                 const void *dO, float *dQ, void *dK, void *dV, int B, int H, int S, int d,
+                 float scale, int causal, void *workspace, size_t workspace_bytes, void *stream) {
+    return fa_bwd_opt(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, S, d, scale, causal, nullptr, workspace,
+                      workspace_bytes, stream);
 }
 
 fa_status fa_exp2_poly(const float *x, float *y, int64_t n, int degree, void *stream) {

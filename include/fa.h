@@ -27,7 +27,9 @@
  *
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
- *     allocates nothing and keeps no state between calls.
+ *     allocates nothing and keeps no mutable state: everything a call uses
+ *     arrives in its arguments (the tuning options as a per-call struct,
+ *     copied on entry), so one call cannot see another's settings.
  *   - Q, K, V, O, dO, dK, dV: bf16 (raw 16-bit patterns), contiguous
  *     row-major [B][H][S][d].  LSE: fp32 [B][H][S].  dQ: fp32 [B][H][S][d].
  *     The backward workspace holds -D (fp32 [B][H][S], D_i = sum_k dO_ik
@@ -38,6 +40,8 @@
  *     nothing.  S <= 2^22 (per-head offsets are 32-bit) and B*H <= 2^31-1.
  *   - scale must be finite and > 0 (1/sqrt(d) is the usual value).
  *   - causal must be 0 or 1.
+ *   - opts (where taken) may be NULL for the defaults of fa_default_options;
+ *     out-of-range fields give FA_ERR_INVALID.
  *   - stream is a hipStream_t (NULL = the default stream).  Calls only
  *     enqueue work and never synchronize; results are ready when the stream
  *     reaches them.  Argument errors are reported synchronously, before
@@ -63,6 +67,38 @@ typedef enum {
     FA_ERR_HIP = 3          /* the HIP runtime refused a launch */
 } fa_status;
 
+/*
+ * Tuning options of one call.  None of them changes the mathematical result
+ * (only rounding, and for the block order not even that).
+ *   rescale_tau: the running row max (in log2 units) is moved, and O and
+ *     the row sum rescaled, only when a new tile's max exceeds it by more
+ *     than tau -- the rescale that is skipped while the numbers do not grow
+ *     too much (gist.science explainer, German page, section 3).  Finite,
+ *     0 <= tau <= 64; 0 rescales on every increase (classic online
+ *     softmax).  Unnormalised probabilities stay below 2^tau.  Default 8.
+ *   poly_eighths: how many eighths (0, 1 or 2) of the forward's
+ *     exponentials use the FMA polynomial exp2 instead of the hardware
+ *     v_exp_f32 (the hybrid split of the technical summary, methodology
+ *     item 2).  Default 0: on gfx950 the hardware exponential costs about two
+ *     FMA slots, the polynomial about seven.
+ *   poly_degree: 3 or 5 (default 3).
+ *   longest_first: causal block order.  1 (default): longest blocks first,
+ *     the LPT order of the technical summary's results (forward and dQ
+ *     kernel: last query blocks first; dK/dV kernel: first key blocks
+ *     first).  0: shortest first, kept for measuring what the order is
+ *     worth.  The result does not depend on it.
+ * The forward reads all four fields, the gradient kernels longest_first.
+ */
+typedef struct fa_options {
+    float rescale_tau;
+    int poly_eighths;
+    int poly_degree;
+    int longest_first;
+} fa_options;
+
+/* The defaults: {8.0f, 0, 3, 1}. */
+fa_options fa_default_options(void);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *fa_status_string(fa_status s);
 
@@ -73,6 +109,11 @@ const char *fa_status_string(fa_status s);
  */
 fa_status fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE,
                  int B, int H, int S, int d, float scale, int causal, void *stream);
+
+/* fa_fwd with explicit tuning options (NULL = defaults). */
+fa_status fa_fwd_opt(const void *Q, const void *K, const void *V, void *O, float *LSE,
+                     int B, int H, int S, int d, float scale, int causal,
+                     const fa_options *opts, void *stream);
 
 /*
  * Forward pass over a packed batch of variable-length sequences (the
@@ -90,13 +131,15 @@ fa_status fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LS
  *   max_seqlen: an upper bound of the sequence lengths (the launch covers
  *     this many rows per sequence; rows of a longer sequence past it are
  *     not written).
- * total * H * d * 2 must stay below 2^32, max_seqlen <= 2^22.  nseq, H,
- * total or max_seqlen equal to 0 is a valid empty call.  Other rules as
- * fa_fwd.  Uses the same softmax options and causal order as fa_fwd.
+ * Row offsets inside one (sequence, head) are 32-bit: with R = max(max_seqlen
+ * rounded up to 256, total + 192) rows (the furthest the kernel's query and
+ * key/value tiles reach), R * H * d * 2 must not exceed 2^32, else
+ * FA_ERR_INVALID.  max_seqlen <= 2^22.  nseq, H, total or max_seqlen equal
+ * to 0 is a valid empty call.  Other rules as fa_fwd_opt.
  */
 fa_status fa_fwd_varlen(const void *Q, const void *K, const void *V, void *O, float *LSE,
                         const int *cu_seqlens, int nseq, int H, int total, int max_seqlen, int d,
-                        float scale, int causal, void *stream);
+                        float scale, int causal, const fa_options *opts, void *stream);
 
 /* Bytes of workspace fa_bwd needs: 2*B*H*S fp32 values (-D and LSE*log2 e). */
 size_t fa_bwd_workspace_bytes(int B, int H, int S, int d);
@@ -110,12 +153,18 @@ size_t fa_bwd_workspace_bytes(int B, int H, int S, int d);
  * entry are ignored and on return are -D and LSE*log2(e).  Outputs must not
  * overlap inputs.
  * Equivalent to fa_bwd_preprocess, then fa_bwd_dkdv and fa_bwd_dq (the two
- * gradient kernels are independent of each other).
+ * gradient kernels are independent of each other), with default options.
  */
 fa_status fa_bwd(const void *Q, const void *K, const void *V, const void *O, const float *LSE,
                  const void *dO, float *dQ, void *dK, void *dV,
                  int B, int H, int S, int d, float scale, int causal,
                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* fa_bwd with explicit options (NULL = defaults). */
+fa_status fa_bwd_opt(const void *Q, const void *K, const void *V, const void *O, const float *LSE,
+                     const void *dO, float *dQ, void *dK, void *dV,
+                     int B, int H, int S, int d, float scale, int causal, const fa_options *opts,
+                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Step 1 of fa_bwd: -D_i = -sum_k dO_ik O_ik and LSE_i * log2(e), fp32, into
@@ -132,7 +181,7 @@ fa_status fa_bwd_preprocess(const void *O, const void *dO, const float *LSE,
  */
 fa_status fa_bwd_dkdv(const void *Q, const void *K, const void *V,
                       const void *dO, void *dK, void *dV,
-                      int B, int H, int S, int d, float scale, int causal,
+                      int B, int H, int S, int d, float scale, int causal, const fa_options *opts,
                       const void *workspace, size_t workspace_bytes, void *stream);
 
 /*
@@ -142,36 +191,8 @@ fa_status fa_bwd_dkdv(const void *Q, const void *K, const void *V,
  */
 fa_status fa_bwd_dq(const void *Q, const void *K, const void *V,
                     const void *dO, float *dQ,
-                    int B, int H, int S, int d, float scale, int causal,
+                    int B, int H, int S, int d, float scale, int causal, const fa_options *opts,
                     const void *workspace, size_t workspace_bytes, void *stream);
-
-/*
- * Tuning knobs of the forward softmax, process-wide, read by every later
- * fa_fwd / fa_bwd call.
- *   rescale_tau: the running row max (in log2 units) is moved, and O and
- *     the row sum rescaled, only when a new tile's max exceeds it by more
- *     than tau.  tau >= 0 and finite; 0 rescales on every increase.  Any
- *     tau gives the same exact result up to rounding; unnormalised
- *     probabilities stay below 2^tau.  Default 8.
- *   poly_eighths: how many eighths (0, 1 or 2) of the exponentials use the
- *     FMA polynomial exp2 instead of the hardware v_exp_f32 (the hybrid
- *     split of the technical summary, methodology item 2).  Default 0: on
- *     gfx950 the hardware exponential costs about two FMA slots, the
- *     polynomial about seven.
- *   poly_degree: 3 or 5.
- * Returns FA_ERR_INVALID for values outside these sets.
- */
-fa_status fa_set_softmax_options(float rescale_tau, int poly_eighths, int poly_degree);
-
-/*
- * Causal block order, process-wide like the softmax options.  1 (default):
- * longest blocks first -- the LPT order of the technical summary's results
- * (forward and dQ kernel: last query blocks first; dK/dV kernel: first key
- * blocks first).  0: the reverse, shortest first, kept for measuring what
- * the order is worth.  The result does not depend on it.  Returns
- * FA_ERR_INVALID for other values.
- */
-fa_status fa_set_causal_order(int longest_first);
 
 /*
  * Diagnostic: y[i] = exp2 of x[i] through the device polynomial of the given

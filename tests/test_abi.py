@@ -87,21 +87,57 @@ def test_backward_checks(lib):
     p[6] = MIS
     assert lib.fa_bwd(*p, 1, 1, 128, 128, ctypes.c_float(0.1), 0, A, 1024, NULL) == 1
     assert lib.fa_bwd(*p9, 1, 1, 128, 64 + 1, ctypes.c_float(0.1), 0, A, 1024, NULL) == 2
-    assert lib.fa_bwd_dkdv(*([A] * 6), 1, 1, 128, 128, ctypes.c_float(0.1), 3, A, 1024, NULL) == 1
-    assert lib.fa_bwd_dkdv(*([A] * 5), MIS, 1, 1, 128, 128, ctypes.c_float(0.1), 0, A, 1024, NULL) == 1
-    assert lib.fa_bwd_dq(*([A] * 4), MIS, 1, 1, 128, 128, ctypes.c_float(0.1), 0, A, 1024, NULL) == 1
-    assert lib.fa_bwd_dq(*([A] * 5), 1, 1, 128, 128, ctypes.c_float(0.0), 0, A, 1024, NULL) == 1
+    assert lib.fa_bwd_dkdv(*([A] * 6), 1, 1, 128, 128, ctypes.c_float(0.1), 3, NULL, A, 1024, NULL) == 1
+    assert lib.fa_bwd_dkdv(*([A] * 5), MIS, 1, 1, 128, 128, ctypes.c_float(0.1), 0, NULL, A, 1024, NULL) == 1
+    assert lib.fa_bwd_dq(*([A] * 4), MIS, 1, 1, 128, 128, ctypes.c_float(0.1), 0, NULL, A, 1024, NULL) == 1
+    assert lib.fa_bwd_dq(*([A] * 5), 1, 1, 128, 128, ctypes.c_float(0.0), 0, NULL, A, 1024, NULL) == 1
     assert lib.fa_bwd_preprocess(A, MIS, A, 1, 1, 128, 128, A, 1024, NULL) == 1
     assert lib.fa_bwd_preprocess(A, A, NULL, 1, 1, 128, 128, A, 1024, NULL) == 1
     assert lib.fa_bwd_preprocess(A, A, A, 1, 1, 128, 128, A, 4, NULL) == 1
 
 
-def test_softmax_options_validation(lib):
-    assert lib.fa_set_softmax_options(ctypes.c_float(-1.0), 0, 3) == 1
-    assert lib.fa_set_softmax_options(ctypes.c_float(8.0), 3, 3) == 1
-    assert lib.fa_set_softmax_options(ctypes.c_float(8.0), 1, 4) == 1
-    assert lib.fa_set_softmax_options(ctypes.c_float(float("nan")), 0, 3) == 1
-    assert lib.fa_set_softmax_options(ctypes.c_float(8.0), 0, 3) == 0
+def test_default_options(lib):
+    import exact_attention_39_amd as fa
+    o = lib.fa_default_options()
+    assert (o.rescale_tau, o.poly_eighths, o.poly_degree, o.longest_first) == (8.0, 0, 3, 1)
+    assert repr(fa.default_options()) == repr(fa.Options())
+
+
+@pytest.mark.parametrize("fields", [(-1.0, 0, 3, 1), (float("nan"), 0, 3, 1), (65.0, 0, 3, 1),
+                                    (8.0, 3, 3, 1), (8.0, -1, 3, 1), (8.0, 1, 4, 1), (8.0, 0, 3, 2)])
+def test_options_out_of_range_are_rejected_by_every_entry_point(lib, fields):
+    """Per-call options are validated on the host, before any HIP call: every
+    entry point that takes them returns FA_ERR_INVALID for a bad field."""
+    import exact_attention_39_amd as fa
+    o = fa.Options()
+    o.rescale_tau, o.poly_eighths, o.poly_degree, o.longest_first = fields
+    po = ctypes.byref(o)
+    f = ctypes.c_float
+    assert lib.fa_fwd_opt(A, A, A, A, A, 1, 1, 128, 128, f(0.1), 0, po, NULL) == 1
+    assert lib.fa_fwd_varlen(A, A, A, A, A, A, 2, 2, 300, 200, 128, f(0.1), 0, po, NULL) == 1
+    assert lib.fa_bwd_opt(*([A] * 9), 1, 1, 128, 128, f(0.1), 0, po, A, 1024, NULL) == 1
+    assert lib.fa_bwd_dkdv(*([A] * 6), 1, 1, 128, 128, f(0.1), 0, po, A, 1024, NULL) == 1
+    assert lib.fa_bwd_dq(*([A] * 5), 1, 1, 128, 128, f(0.1), 0, po, A, 1024, NULL) == 1
+    # bad options are rejected even for empty calls (nothing else is looked at)
+    assert lib.fa_fwd_opt(*([NULL] * 5), 1, 1, 0, 128, f(0.1), 0, po, NULL) == 1
+
+
+def test_options_are_read_once_per_call_no_shared_state(lib):
+    """The library holds no tuning state: a call with NULL options behaves as
+    the defaults whatever other calls passed before (here: a valid non-default
+    set, then an invalid one, then NULL on an empty call)."""
+    import exact_attention_39_amd as fa
+    f = ctypes.c_float
+    odd = fa.Options(0.0, 2, 5, False)
+    assert lib.fa_fwd_opt(*([NULL] * 5), 1, 1, 0, 128, f(0.1), 0, ctypes.byref(odd), NULL) == 0
+    bad = fa.Options(8.0, 7, 3, True)
+    assert lib.fa_fwd_opt(*([NULL] * 5), 1, 1, 0, 128, f(0.1), 0, ctypes.byref(bad), NULL) == 1
+    assert lib.fa_fwd_opt(*([NULL] * 5), 1, 1, 0, 128, f(0.1), 0, NULL, NULL) == 0
+    assert "fa_set_softmax_options" not in declared_functions()
+    assert "fa_set_causal_order" not in declared_functions()
+
+
+def test_exp2_poly_validation(lib):
     assert lib.fa_exp2_poly(NULL, NULL, -1, 3, NULL) == 1
     assert lib.fa_exp2_poly(NULL, NULL, 0, 3, NULL) == 0
     assert lib.fa_exp2_poly(A, A, 16, 4, NULL) == 1
@@ -117,18 +153,37 @@ def test_binding_refuses_cpu_tensors():
 
 def fwd_varlen(lib, nseq=2, H=2, total=300, max_seqlen=200, d=128, scale=0.088, causal=0, ptrs=None, cu=A):
     p = ptrs or [A, A, A, A, A]
-    return lib.fa_fwd_varlen(*p, cu, nseq, H, total, max_seqlen, d, ctypes.c_float(scale), causal, NULL)
+    return lib.fa_fwd_varlen(*p, cu, nseq, H, total, max_seqlen, d, ctypes.c_float(scale), causal, NULL, NULL)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(nseq=-1), 1), (dict(H=-1), 1), (dict(total=-3), 1), (dict(max_seqlen=-1), 1),
     (dict(d=80), 2), (dict(scale=0.0), 1), (dict(scale=float("nan")), 1), (dict(causal=2), 1),
     (dict(max_seqlen=(1 << 22) + 1), 1),
-    # total * H * d * 2 must stay below 2^32
+    # row offsets of one (sequence, head) must stay below 2^32
     (dict(total=1 << 20, H=16), 1),
+    # the furthest query block: max_seqlen rounded up to 256 rows, at H*d*2 bytes per row
+    (dict(total=300, max_seqlen=(1 << 22), H=8, d=128), 1),
+    # one sequence of 2,796,202 tokens at H = 12, d = 64: total * H * d * 2 < 2^32, but the key/value
+    # tile copies reach 192 rows past the end, whose offsets would wrap onto the first rows
+    (dict(nseq=1, total=2796202, max_seqlen=2796202, H=12, d=64), 1),
 ])
 def test_varlen_forward_rejects_bad_arguments(lib, kw, code):
     assert fwd_varlen(lib, **kw) == code
+
+
+def test_varlen_offset_bound_is_tight(lib):
+    """The largest accepted packed batch has every row offset the kernel forms
+    below 2^32: reach = max(round_up(max_seqlen, 256), total + 192) rows of
+    H*d*2 bytes.  One token more is rejected (fake pointers: a call that passes
+    the checks would launch, so only the rejected side runs here)."""
+    H, d = 12, 64
+    pitch = H * d * 2
+    total_ok = (1 << 32) // pitch - 192
+    assert (total_ok + 192) * pitch <= (1 << 32) < (total_ok + 193) * pitch
+    assert fwd_varlen(lib, nseq=1, total=total_ok + 1, max_seqlen=total_ok + 1, H=H, d=d) == 1
+    maxlen_bad = (1 << 32) // pitch // 256 * 256 + 1     # rounds up past the limit
+    assert fwd_varlen(lib, nseq=1, total=100, max_seqlen=maxlen_bad, H=H, d=d) == 1
 
 
 def test_varlen_forward_null_misaligned_and_empty(lib):

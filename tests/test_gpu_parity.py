@@ -39,7 +39,6 @@ def fa():
         pytest.fail("no GPU visible: the -m gpu tests need an MI355X")
     import exact_attention_39_amd as m
     m.load_library()
-    m.fa_set_softmax_options(8.0, 0, 3)
     return m
 
 
@@ -79,9 +78,9 @@ def check_grad(g, ref, what):
     return rel
 
 
-def run_fwd(fa, qb, kb, vb, causal, scale):
+def run_fwd(fa, qb, kb, vb, causal, scale, opts=None):
     q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
-    o, lse = fa.forward(q, k, v, causal=causal, scale=scale)
+    o, lse = fa.forward(q, k, v, causal=causal, scale=scale, opts=opts)
     torch.cuda.synchronize()
     return q, k, v, o, lse
 
@@ -177,18 +176,15 @@ def test_forward_repeatable_and_rescale_options_agree(fa, d):
     scale = 1.0 / np.sqrt(d)
     Q, K, V = (gen.bf16_bits_to_f64(x) for x in (qb, kb, vb))
     refs = {c: oracle.attention_forward(Q, K, V, scale, c) for c in (False, True)}
-    try:
-        for tau, poly, deg in [(8.0, 0, 3), (0.0, 0, 3), (8.0, 1, 3), (8.0, 2, 3), (8.0, 2, 5), (2.0, 1, 5)]:
-            fa.fa_set_softmax_options(tau, poly, deg)
-            for causal in (False, True):
-                _, _, _, o, lse = run_fwd(fa, qb, kb, vb, causal, scale)
-                what = f"tau={tau} poly={poly}/8 deg={deg} causal={causal}"
-                check_o(bf16_to_np64(o), refs[causal][0], what)
-                check_lse(lse.cpu().numpy().astype(np.float64), refs[causal][1], what)
-                _, _, _, o2, lse2 = run_fwd(fa, qb, kb, vb, causal, scale)
-                assert torch.equal(o, o2) and torch.equal(lse, lse2), f"{what}: not repeatable"
-    finally:
-        fa.fa_set_softmax_options(8.0, 0, 3)
+    for tau, poly, deg in [(8.0, 0, 3), (0.0, 0, 3), (8.0, 1, 3), (8.0, 2, 3), (8.0, 2, 5), (2.0, 1, 5)]:
+        opts = fa.Options(tau, poly, deg)
+        for causal in (False, True):
+            _, _, _, o, lse = run_fwd(fa, qb, kb, vb, causal, scale, opts)
+            what = f"tau={tau} poly={poly}/8 deg={deg} causal={causal}"
+            check_o(bf16_to_np64(o), refs[causal][0], what)
+            check_lse(lse.cpu().numpy().astype(np.float64), refs[causal][1], what)
+            _, _, _, o2, lse2 = run_fwd(fa, qb, kb, vb, causal, scale, opts)
+            assert torch.equal(o, o2) and torch.equal(lse, lse2), f"{what}: not repeatable"
 
 
 def test_reference_max_paths(fa):
@@ -205,34 +201,29 @@ def test_reference_max_paths(fa):
     kb, vb = rand_bits(shape, 91), rand_bits(shape, 92)
     V = gen.bf16_bits_to_f64(vb)
     zero = np.zeros(shape, dtype=np.uint16)  # bf16 +0.0
-    try:
-        for tau in (8.0, 2.0, 0.0):
-            fa.fa_set_softmax_options(tau, 0, 3)
-            for causal in (False, True):
-                _, _, _, o, lse = run_fwd(fa, zero, kb, vb, causal, scale)
-                cnt = np.arange(1, S + 1, dtype=np.float64) if causal else np.full(S, float(S))
-                o_ref = (np.cumsum(V, axis=2) / cnt[:, None]) if causal else np.broadcast_to(V.mean(axis=2, keepdims=True), shape)
-                what = f"Q=0 tau={tau} causal={causal}"
-                check_o(bf16_to_np64(o), o_ref, what)
-                check_lse(lse.cpu().numpy().astype(np.float64), np.broadcast_to(np.log(cnt), (B, H, S)), what)
-        # late jump: keys S-50.. get +96 on every raw score (12 in log2 units)
-        q = gen.bf16_bits_to_f64(rand_bits(shape, 93)).astype(np.float32)
-        k = gen.bf16_bits_to_f64(kb).astype(np.float32)
-        q[..., 0] = 8.0
-        k[..., : S - 50, 0] = 0.0
-        k[..., S - 50:, 0] = 12.0
-        qb2, kb2 = gen.f32_to_bf16_bits(q), gen.f32_to_bf16_bits(k)
-        Q2, K2 = gen.bf16_bits_to_f64(qb2), gen.bf16_bits_to_f64(kb2)
-        for tau in (8.0, 2.0):
-            fa.fa_set_softmax_options(tau, 0, 3)
-            for causal in (False, True):
-                o_ref, l_ref = oracle.attention_forward(Q2, K2, V, scale, causal)
-                _, _, _, o, lse = run_fwd(fa, qb2, kb2, vb, causal, scale)
-                what = f"late jump tau={tau} causal={causal}"
-                check_o(bf16_to_np64(o), o_ref, what)
-                check_lse(lse.cpu().numpy().astype(np.float64), l_ref, what)
-    finally:
-        fa.fa_set_softmax_options(8.0, 0, 3)
+    for tau in (8.0, 2.0, 0.0):
+        for causal in (False, True):
+            _, _, _, o, lse = run_fwd(fa, zero, kb, vb, causal, scale, fa.Options(tau))
+            cnt = np.arange(1, S + 1, dtype=np.float64) if causal else np.full(S, float(S))
+            o_ref = (np.cumsum(V, axis=2) / cnt[:, None]) if causal else np.broadcast_to(V.mean(axis=2, keepdims=True), shape)
+            what = f"Q=0 tau={tau} causal={causal}"
+            check_o(bf16_to_np64(o), o_ref, what)
+            check_lse(lse.cpu().numpy().astype(np.float64), np.broadcast_to(np.log(cnt), (B, H, S)), what)
+    # late jump: keys S-50.. get +96 on every raw score (12 in log2 units)
+    q = gen.bf16_bits_to_f64(rand_bits(shape, 93)).astype(np.float32)
+    k = gen.bf16_bits_to_f64(kb).astype(np.float32)
+    q[..., 0] = 8.0
+    k[..., : S - 50, 0] = 0.0
+    k[..., S - 50:, 0] = 12.0
+    qb2, kb2 = gen.f32_to_bf16_bits(q), gen.f32_to_bf16_bits(k)
+    Q2, K2 = gen.bf16_bits_to_f64(qb2), gen.bf16_bits_to_f64(kb2)
+    for tau in (8.0, 2.0):
+        for causal in (False, True):
+            o_ref, l_ref = oracle.attention_forward(Q2, K2, V, scale, causal)
+            _, _, _, o, lse = run_fwd(fa, qb2, kb2, vb, causal, scale, fa.Options(tau))
+            what = f"late jump tau={tau} causal={causal}"
+            check_o(bf16_to_np64(o), o_ref, what)
+            check_lse(lse.cpu().numpy().astype(np.float64), l_ref, what)
 
 
 def test_device_exp2_polynomial(fa):
@@ -307,6 +298,23 @@ def test_workload_forward_sampled(fa, name, causal):
         check_lse(l_g, l_ref, f"{name} head ({b},{h})")
 
 
+@pytest.mark.parametrize("name,causal", [("fwd_b4_h16_s4096", False), ("causal_boost_b2_h16_s8192", True)])
+def test_workload_forward_full_tensors(fa, name, causal):
+    """Every element of O and LSE of the two forward-only workloads against the
+    oracle's full forward (its cost, 5.5e11 and 2.8e11 fp64 FLOP, is seconds),
+    so the O mean-abs criterion runs over all elements."""
+    say(f"[workload fwd full] {name} causal={causal}")
+    w = gen.WORKLOADS[name]
+    bits = workload_bits(name)
+    scale = gen.default_scale(w["d"])
+    _, _, _, o, lse = run_fwd(fa, bits["q"], bits["k"], bits["v"], causal, scale)
+    Q, K, V = (gen.bf16_bits_to_f64(bits[t]) for t in "qkv")
+    o_ref, l_ref = oracle.attention_forward(Q, K, V, scale, causal)
+    del Q, K, V
+    check_o(bf16_to_np64(o), o_ref, f"{name} all elements")
+    check_lse(lse.cpu().numpy().astype(np.float64), l_ref, f"{name} all elements")
+
+
 WORKLOAD_BWD = [
     ("fwd_b4_h16_s4096", False),
     ("causal_boost_b2_h16_s8192", True),  # every 64th query row x8: peaked rows
@@ -318,6 +326,9 @@ WORKLOAD_BWD = [
 
 @pytest.mark.parametrize("name,causal", WORKLOAD_BWD)
 def test_workload_backward_sampled(fa, name, causal):
+    """Sampled dQ rows of every head (cheap for the oracle: S*d work per row)
+    and sampled dK/dV key rows of the first, a middle and the last head (each
+    needs the full softmax of its head)."""
     say(f"[workload bwd] {name} causal={causal}")
     w = gen.WORKLOADS[name]
     bits = workload_bits(name)
@@ -326,18 +337,22 @@ def test_workload_backward_sampled(fa, name, causal):
     do = to_dev(bits["do"])
     dq, dk, dv = fa.backward(q, k, v, o, lse, do, causal=causal, scale=scale)
     torch.cuda.synchronize()
-    S = w["S"]
-    b, h = w["B"] - 1, w["H"] - 1
-    Q, K, V, dO = (head_f64(bits[t], b, h) for t in ("q", "k", "v", "do"))
+    S, B, H = w["S"], w["B"], w["H"]
     rows = sample_rows(S)
-    gq = oracle.backward_dq_rows(Q, K, V, dO, rows, scale, causal)
     idx = torch.from_numpy(rows).cuda()
-    check_grad(dq[b, h, idx].cpu().numpy().astype(np.float64), gq, f"{name} dQ rows")
+    dq_rows = dq[:, :, idx].cpu().numpy().astype(np.float64)
+    for b in range(B):
+        for h in range(H):
+            Q, K, V, dO = (head_f64(bits[t], b, h) for t in ("q", "k", "v", "do"))
+            gq = oracle.backward_dq_rows(Q, K, V, dO, rows, scale, causal)
+            check_grad(dq_rows[b, h], gq, f"{name} dQ rows head ({b},{h})")
     cols = np.array(sorted({0, 1, 127, 128, S // 3, S // 2, S - 129, S - 128, S - 1}), dtype=np.int64)
-    gk, gv = oracle.backward_dkdv_cols(Q, K, V, dO, cols, scale, causal)
     cidx = torch.from_numpy(cols).cuda()
-    check_grad(bf16_to_np64(dk[b, h, cidx]), gk, f"{name} dK cols")
-    check_grad(bf16_to_np64(dv[b, h, cidx]), gv, f"{name} dV cols")
+    for b, h in sorted({(0, 0), (B // 2, H // 2), (B - 1, H - 1)}):
+        Q, K, V, dO = (head_f64(bits[t], b, h) for t in ("q", "k", "v", "do"))
+        gk, gv = oracle.backward_dkdv_cols(Q, K, V, dO, cols, scale, causal)
+        check_grad(bf16_to_np64(dk[b, h, cidx]), gk, f"{name} dK cols head ({b},{h})")
+        check_grad(bf16_to_np64(dv[b, h, cidx]), gv, f"{name} dV cols head ({b},{h})")
 
 
 @pytest.mark.parametrize("B,H,S,d,causal", [(2, 3, 3000, 64, False), (2, 3, 3000, 64, True),
@@ -384,6 +399,72 @@ def test_backward_is_bitwise_repeatable(fa):
         torch.cuda.synchronize()
         for a, b, nm in zip(g1, g2, ("dQ", "dK", "dV")):
             assert torch.equal(a, b), f"{nm} differs between runs (causal={causal})"
+
+
+def test_options_do_not_mix_across_threads(fa):
+    """Options travel with each call.  Two host threads launch forwards with
+    different options on their own streams at the same time; every result is
+    bitwise the one that option set gives alone (the polynomial exp2 and the
+    max-first order change the rounding, so a mixed-up call would show)."""
+    import threading
+    say("[threads] per-call options")
+    shape = (1, 4, 1024, 128)
+    qb, kb, vb = (rand_bits(shape, 300 + i, scale=2.0) for i in range(3))
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    scale = 1.0 / np.sqrt(128)
+    sets = [fa.Options(8.0, 0, 3), fa.Options(0.0, 2, 5), fa.Options(2.0, 1, 3, False)]
+    ref = []
+    for opts in sets:
+        o, lse = fa.forward(q, k, v, causal=True, scale=scale, opts=opts)
+        torch.cuda.synchronize()
+        ref.append((o.clone(), lse.clone()))
+    assert not torch.equal(ref[0][0], ref[1][0]), "option sets must give distinguishable bits"
+    errors = []
+
+    def worker(t):
+        opts = sets[t]
+        st = torch.cuda.Stream()
+        try:
+            for _ in range(20):
+                o, lse = fa.forward(q, k, v, causal=True, scale=scale, opts=opts, stream=st)
+                st.synchronize()
+                if not (torch.equal(o, ref[t][0]) and torch.equal(lse, ref[t][1])):
+                    errors.append(t)
+        except Exception as e:  # pragma: no cover - reported below
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(len(sets))]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+
+
+def test_backward_on_a_side_stream(fa):
+    """backward() allocates its outputs and workspace on the stream it
+    launches on.  With the kernels queued on a side stream and new
+    allocations made on the current stream before any synchronisation, the
+    gradients are bitwise those of a run on the current stream."""
+    say("[stream] backward on a side stream")
+    shape = (2, 4, 2000, 128)
+    qb, kb, vb, db = (rand_bits(shape, 400 + i) for i in range(4))
+    scale = 1.0 / np.sqrt(128)
+    q, k, v, o, lse = run_fwd(fa, qb, kb, vb, True, scale)
+    do = to_dev(db)
+    ref = fa.backward(q, k, v, o, lse, do, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        got = fa.backward(q, k, v, o, lse, do, causal=True, scale=scale, stream=side)
+        # allocations and writes on the current stream while the side stream still runs
+        junk = [torch.full((fa.fa_bwd_workspace_bytes(*shape) // 4,), 7.0, device="cuda") for _ in range(4)]
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        del junk
+        for a, b, nm in zip(got, ref, ("dQ", "dK", "dV")):
+            assert torch.equal(a, b), f"{nm} differs on the side stream"
 
 
 # ------------------------------------------------------------------ packed variable-length forward
@@ -437,25 +518,22 @@ def test_varlen_softmax_options(fa, d):
     scale = 1.0 / np.sqrt(d)
     q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
     cu_d = torch.from_numpy(cu).cuda()
-    try:
-        for tau, poly, deg in [(0.0, 2, 5), (2.0, 1, 3)]:
-            fa.fa_set_softmax_options(tau, poly, deg)
-            for causal in (False, True):
-                say(f"[varlen options] d={d} tau={tau} poly={poly}/8 deg={deg} causal={causal}")
-                o, lse = fa.forward_varlen(q, k, v, cu_d, max(lens), causal=causal, scale=scale)
-                torch.cuda.synchronize()
-                o_np, lse_np = bf16_to_np64(o), lse.cpu().numpy().astype(np.float64)
-                for sq in range(len(lens)):
-                    a, b = int(cu[sq]), int(cu[sq + 1])
-                    if a == b:
-                        continue
-                    o_ref, lse_ref = oracle.attention_forward(seq_f64(qb, a, b), seq_f64(kb, a, b),
-                                                              seq_f64(vb, a, b), scale, causal)
-                    what = f"varlen seq {sq} tau={tau} poly={poly} deg={deg} causal={causal}"
-                    check_o(o_np[a:b].transpose(1, 0, 2), o_ref[0], what)
-                    check_lse(lse_np[:, a:b], lse_ref[0], what)
-    finally:
-        fa.fa_set_softmax_options(8.0, 0, 3)
+    for tau, poly, deg in [(0.0, 2, 5), (2.0, 1, 3)]:
+        for causal in (False, True):
+            say(f"[varlen options] d={d} tau={tau} poly={poly}/8 deg={deg} causal={causal}")
+            o, lse = fa.forward_varlen(q, k, v, cu_d, max(lens), causal=causal, scale=scale,
+                                       opts=fa.Options(tau, poly, deg))
+            torch.cuda.synchronize()
+            o_np, lse_np = bf16_to_np64(o), lse.cpu().numpy().astype(np.float64)
+            for sq in range(len(lens)):
+                a, b = int(cu[sq]), int(cu[sq + 1])
+                if a == b:
+                    continue
+                o_ref, lse_ref = oracle.attention_forward(seq_f64(qb, a, b), seq_f64(kb, a, b),
+                                                          seq_f64(vb, a, b), scale, causal)
+                what = f"varlen seq {sq} tau={tau} poly={poly} deg={deg} causal={causal}"
+                check_o(o_np[a:b].transpose(1, 0, 2), o_ref[0], what)
+                check_lse(lse_np[:, a:b], lse_ref[0], what)
 
 
 def test_varlen_equals_dense_forward_bitwise(fa):
@@ -509,25 +587,22 @@ def test_varlen_many_sequences_and_work_order(fa):
     scale = 1.0 / np.sqrt(d)
     q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
     cu_d = torch.from_numpy(cu).cuda()
-    try:
-        for causal in (False, True):
-            fa.fa_set_causal_order(True)
-            o, lse = fa.forward_varlen(q, k, v, cu_d, max(lens), causal=causal, scale=scale)
-            fa.fa_set_causal_order(False)
-            o2, lse2 = fa.forward_varlen(q, k, v, cu_d, max(lens), causal=causal, scale=scale)
-            torch.cuda.synchronize()
-            assert torch.equal(o, o2) and torch.equal(lse, lse2), f"work order changed the result (causal={causal})"
-            o_np, lse_np = bf16_to_np64(o), lse.cpu().numpy().astype(np.float64)
-            for si in range(len(lens)):
-                a, b = int(cu[si]), int(cu[si + 1])
-                if a == b:
-                    continue
-                o_ref, lse_ref = oracle.attention_forward(seq_f64(qb, a, b), seq_f64(kb, a, b), seq_f64(vb, a, b),
-                                                          scale, causal)
-                check_o(o_np[a:b].transpose(1, 0, 2), o_ref[0], f"seq {si} (len {b - a}, causal={causal})")
-                check_lse(lse_np[:, a:b], lse_ref[0], f"seq {si} (len {b - a}, causal={causal})")
-    finally:
-        fa.fa_set_causal_order(True)
+    for causal in (False, True):
+        o, lse = fa.forward_varlen(q, k, v, cu_d, max(lens), causal=causal, scale=scale,
+                                   opts=fa.Options(longest_first=True))
+        o2, lse2 = fa.forward_varlen(q, k, v, cu_d, max(lens), causal=causal, scale=scale,
+                                     opts=fa.Options(longest_first=False))
+        torch.cuda.synchronize()
+        assert torch.equal(o, o2) and torch.equal(lse, lse2), f"work order changed the result (causal={causal})"
+        o_np, lse_np = bf16_to_np64(o), lse.cpu().numpy().astype(np.float64)
+        for si in range(len(lens)):
+            a, b = int(cu[si]), int(cu[si + 1])
+            if a == b:
+                continue
+            o_ref, lse_ref = oracle.attention_forward(seq_f64(qb, a, b), seq_f64(kb, a, b), seq_f64(vb, a, b),
+                                                      scale, causal)
+            check_o(o_np[a:b].transpose(1, 0, 2), o_ref[0], f"seq {si} (len {b - a}, causal={causal})")
+            check_lse(lse_np[:, a:b], lse_ref[0], f"seq {si} (len {b - a}, causal={causal})")
 
 
 def test_varlen_rows_past_max_seqlen_untouched(fa):
@@ -590,14 +665,11 @@ def test_causal_block_order_does_not_change_results(fa):
     qb, kb, vb, db = (rand_bits(shape, 600 + i) for i in range(4))
     scale = 1.0 / np.sqrt(128)
     out = []
-    try:
-        for lpt in (True, False):
-            fa.fa_set_causal_order(lpt)
-            q, k, v, o, lse = run_fwd(fa, qb, kb, vb, True, scale)
-            g = fa.backward(q, k, v, o, lse, to_dev(db), causal=True, scale=scale)
-            torch.cuda.synchronize()
-            out.append((o, lse) + tuple(g))
-    finally:
-        fa.fa_set_causal_order(True)
+    for lpt in (True, False):
+        opts = fa.Options(longest_first=lpt)
+        q, k, v, o, lse = run_fwd(fa, qb, kb, vb, True, scale, opts)
+        g = fa.backward(q, k, v, o, lse, to_dev(db), causal=True, scale=scale, opts=opts)
+        torch.cuda.synchronize()
+        out.append((o, lse) + tuple(g))
     for a, b, nm in zip(out[0], out[1], ("O", "LSE", "dQ", "dK", "dV")):
         assert torch.equal(a, b), f"{nm} depends on the causal block order"

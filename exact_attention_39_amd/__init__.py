@@ -19,7 +19,8 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libfa.so")
 
-FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_TOO_LARGE = 0, 1, 2, 3, 4
+NOALLOC_SCRATCH_BYTES = 16 << 20  # FA_NOALLOC_SCRATCH_BYTES of include/fa.h
 
 _lib = None
 
@@ -71,6 +72,8 @@ def load_library():
     lib.fa_bwd.restype = i
     lib.fa_bwd_opt.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, op, vp, sz, vp]
     lib.fa_bwd_opt.restype = i
+    lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+    lib.fa_bwd_noalloc.restype = i
     lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, vp, sz, vp]
     lib.fa_bwd_preprocess.restype = i
     lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, op, vp, sz, vp]
@@ -189,6 +192,15 @@ def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, scale: float, causal: bool, workspac
     _check(load_library().fa_bwd_opt(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
                                      _ptr(dk), _ptr(dv), B, H, S, d, float(scale), int(bool(causal)),
                                      _opts(opts), _ptr(workspace), ws_bytes, _stream(stream)), "fa_bwd")
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, scale: float, causal: bool, stream=None):
+    """fa_bwd with the library's static device workspace: allocates nothing.
+    Calls that overlap on one GPU race on that workspace."""
+    B, H, S, d = _bwd_checks(q, k, v, o, lse, do, dq, dk, dv)
+    _check(load_library().fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
+                                         _ptr(dk), _ptr(dv), B, H, S, d, float(scale), int(bool(causal)),
+                                         _stream(stream)), "fa_bwd_noalloc")
 
 
 def fa_bwd_preprocess(o, do, lse, workspace, stream=None):

@@ -6,6 +6,8 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "exp2_poly.h"
 #include "fa.h"
@@ -72,7 +74,10 @@ const char *fa_status_string(fa_status s) {
         case FA_OK: return "FA_OK";
         case FA_ERR_INVALID: return "FA_ERR_INVALID: invalid argument";
         case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dimension must be 64 or 128";
-        case FA_ERR_HIP: return "FA_ERR_HIP: kernel launch failed";
+        case FA_ERR_HIP: return "FA_ERR_HIP: kernel launch or device symbol lookup failed";
+        case FA_ERR_TOO_LARGE:
+            return "FA_ERR_TOO_LARGE: the workspace (2*B*H*S*4 bytes) exceeds the static scratch array "
+                   "of fa_bwd_noalloc (FA_NOALLOC_SCRATCH_BYTES)";
     }
     return "unknown fa_status";
 }
@@ -250,6 +255,67 @@ fa_status fa_bwd(const void *Q, const void *K, const void *V, const void *O, con
                  float scale, int causal, void *workspace, size_t workspace_bytes, void *stream) {
     return fa_bwd_opt(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, S, d, scale, causal, nullptr, workspace,
                       workspace_bytes, stream);
+}
+
+// ------------------------------------------------------------ no-allocation backward
+// The workspace of fa_bwd_noalloc: one array per GPU the library runs on,
+// held until the process ends.  In host code `scratch` only names the
+// symbol; its device address comes from hipGetSymbolAddress, once per
+// device, with that device current, and only that address is passed on.
+static __device__ __align__(256) char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device, looked up on the first
+// call there; nullptr (and *err set) if the lookup fails.
+void *scratch_address(hipError_t *err) {
+    int dev = -1;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (*err != hipSuccess || !p) {
+            if (*err == hipSuccess) *err = hipErrorInvalidSymbol;
+            return nullptr;
+        }
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+}  // namespace
+
+fa_status fa_bwd_noalloc(const void *Q, const void *K, const void *V, const void *O, const float *LSE,
+                         const void *dO, float *dQ, void *dK, void *dV, int B, int H, int S, int d,
+                         float scale, int causal, void *stream) {
+    // Host checks first (no HIP call for a malformed or oversized call).
+    bool empty = false;
+    fa_status st = check_shape(B, H, S, d, &empty);
+    if (st != FA_OK) return st;
+    if (!good_scale(scale) || (causal != 0 && causal != 1)) return FA_ERR_INVALID;
+    if (empty) return FA_OK;
+    const size_t need = fa_bwd_workspace_bytes(B, H, S, d);
+    if (need > (size_t)FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_TOO_LARGE;
+    const void *ptrs[] = {Q, K, V, O, LSE, dO, dQ, dK, dV};
+    for (const void *p : ptrs)
+        if (!p || !aligned16(p)) return FA_ERR_INVALID;
+    hipError_t err = hipSuccess;
+    void *ws = scratch_address(&err);
+    if (!ws) return FA_ERR_HIP;
+    // Every element of the workspace that the gradient kernels read is
+    // written by the preprocess step of this call first: nothing to clear.
+    return fa_bwd_opt(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, S, d, scale, causal, nullptr, ws, need,
+                      stream);
 }
 
 fa_status fa_exp2_poly(const float *x, float *y, int64_t n, int degree, void *stream) {

@@ -64,7 +64,8 @@ typedef enum {
     FA_OK = 0,
     FA_ERR_INVALID = 1,     /* null/misaligned pointer, bad size, scale or flag */
     FA_ERR_UNSUPPORTED = 2, /* head dimension other than 64 or 128 */
-    FA_ERR_HIP = 3          /* the HIP runtime refused a launch */
+    FA_ERR_HIP = 3,         /* the HIP runtime refused a launch or a device symbol lookup */
+    FA_ERR_TOO_LARGE = 4    /* fa_bwd_noalloc: the workspace would not fit its static array */
 } fa_status;
 
 /*
@@ -193,6 +194,29 @@ fa_status fa_bwd_dq(const void *Q, const void *K, const void *V,
                     const void *dO, float *dQ,
                     int B, int H, int S, int d, float scale, int causal, const fa_options *opts,
                     const void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): fa_bwd
+ * with its workspace taken from a static device array of the library,
+ * FA_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU, held by each GPU the library
+ * runs on until the process ends.  Same arguments and results as fa_bwd
+ * (default options), minus the workspace; it allocates nothing.
+ *   - Limit: fa_bwd_workspace_bytes(B, H, S, d) = 8*B*H*S bytes must not
+ *     exceed FA_NOALLOC_SCRATCH_BYTES (B*H*S <= 2^21 rows), else
+ *     FA_ERR_TOO_LARGE, reported before any HIP call.
+ *   - The array's device address is looked up (hipGetSymbolAddress) on the
+ *     first call on each device, with that device current; a failed lookup
+ *     gives FA_ERR_HIP.
+ *   - All calls on one GPU share its array, which keeps the last call's
+ *     contents (-D and LSE*log2 e).  Calls that overlap on one GPU (on
+ *     different streams, or from several threads without ordering) race on
+ *     it and give wrong gradients; order them on one stream.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (16u << 20)
+fa_status fa_bwd_noalloc(const void *Q, const void *K, const void *V, const void *O, const float *LSE,
+                         const void *dO, float *dQ, void *dK, void *dV,
+                         int B, int H, int S, int d, float scale, int causal, void *stream);
 
 /*
  * Diagnostic: y[i] = exp2 of x[i] through the device polynomial of the given

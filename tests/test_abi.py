@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(4):
+    for code in range(5):
         assert lib.fa_status_string(code).decode().startswith("FA_")
 
 
@@ -216,3 +216,26 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "not supported" in r.stderr and r.stdout == ""
+
+
+def test_noalloc_backward_host_checks(lib):
+    """fa_bwd_noalloc rejects a workspace larger than its static array
+    (FA_ERR_TOO_LARGE = 4), and malformed calls, on the host before any HIP
+    call; empty calls are no-ops."""
+    import exact_attention_39_amd as fa
+    f = ctypes.c_float
+    p9 = [A] * 9
+    rows_max = fa.NOALLOC_SCRATCH_BYTES // 8           # 8 bytes of workspace per (b, h, query row)
+    assert rows_max == 1 << 21
+    assert lib.fa_bwd_noalloc(*p9, 1, 1, rows_max + 1, 128, f(0.1), 0, NULL) == 4
+    assert lib.fa_bwd_noalloc(*p9, 2, 16, 65537, 128, f(0.1), 1, NULL) == 4
+    assert lib.fa_bwd_noalloc(*p9, 1, 1, 128, 96, f(0.1), 0, NULL) == 2
+    assert lib.fa_bwd_noalloc(*p9, 1, 1, 128, 128, f(0.0), 0, NULL) == 1
+    assert lib.fa_bwd_noalloc(*p9, 1, 1, 128, 128, f(0.1), 2, NULL) == 1
+    p = list(p9)
+    p[6] = MIS
+    assert lib.fa_bwd_noalloc(*p, 1, 1, 128, 128, f(0.1), 0, NULL) == 1
+    p[6] = NULL
+    assert lib.fa_bwd_noalloc(*p, 1, 1, 128, 128, f(0.1), 0, NULL) == 1
+    assert lib.fa_bwd_noalloc(*([NULL] * 9), 1, 1, 0, 128, f(0.1), 0, NULL) == 0
+    assert "scratch" in lib.fa_status_string(4).decode()

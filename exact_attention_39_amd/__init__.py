@@ -28,15 +28,17 @@ _lib = None
 class Options(ctypes.Structure):
     """Per-call tuning options (struct fa_options of include/fa.h)."""
     _fields_ = [("rescale_tau", ctypes.c_float), ("poly_eighths", ctypes.c_int),
-                ("poly_degree", ctypes.c_int), ("longest_first", ctypes.c_int)]
+                ("poly_degree", ctypes.c_int), ("longest_first", ctypes.c_int), ("fused_backward", ctypes.c_int)]
 
     def __init__(self, rescale_tau: float = 8.0, poly_eighths: int = 0, poly_degree: int = 3,
-                 longest_first: bool = True):
-        super().__init__(float(rescale_tau), int(poly_eighths), int(poly_degree), int(bool(longest_first)))
+                 longest_first: bool = True, fused_backward: bool = False):
+        super().__init__(float(rescale_tau), int(poly_eighths), int(poly_degree), int(bool(longest_first)),
+                         int(bool(fused_backward)))
 
     def __repr__(self):
         return (f"Options(rescale_tau={self.rescale_tau}, poly_eighths={self.poly_eighths}, "
-                f"poly_degree={self.poly_degree}, longest_first={bool(self.longest_first)})")
+                f"poly_degree={self.poly_degree}, longest_first={bool(self.longest_first)}, "
+                f"fused_backward={bool(self.fused_backward)})")
 
 
 class FaError(RuntimeError):
@@ -80,6 +82,8 @@ def load_library():
     lib.fa_bwd_dkdv.restype = i
     lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, op, vp, sz, vp]
     lib.fa_bwd_dq.restype = i
+    lib.fa_bwd_fused.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_bwd_fused.restype = i
     lib.fa_exp2_poly.argtypes = [vp, vp, ctypes.c_int64, i, vp]
     lib.fa_exp2_poly.restype = i
     _lib = lib
@@ -243,6 +247,20 @@ def fa_bwd_dq(q, k, v, do, dq, scale: float, causal: bool, workspace, stream=Non
     _check(load_library().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), B, H, S, d,
                                     float(scale), int(bool(causal)), _opts(opts), _ptr(workspace), ws_bytes,
                                     _stream(stream)), "fa_bwd_dq")
+
+
+def fa_bwd_fused(q, k, v, do, dq, dk, dv, scale: float, causal: bool, workspace, stream=None):
+    """dQ, dK, dV in one pass (the single-pass backward) from the workspace
+    that fa_bwd_preprocess filled on the same stream."""
+    import torch
+    B, H, S, d = _grad_checks(q, k, v, do)
+    _check_tensor(dq, "dq", torch.float32, (B, H, S, d))
+    _check_tensor(dk, "dk", torch.bfloat16, (B, H, S, d))
+    _check_tensor(dv, "dv", torch.bfloat16, (B, H, S, d))
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load_library().fa_bwd_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
+                                       B, H, S, d, float(scale), int(bool(causal)), _ptr(workspace), ws_bytes,
+                                       _stream(stream)), "fa_bwd_fused")
 
 
 def fa_exp2_poly(x, y, degree: int = 3, stream=None):

@@ -16,7 +16,7 @@
 
 namespace {
 
-constexpr fa_options kDefaultOptions = {8.0f, 0, 3, 1};
+constexpr fa_options kDefaultOptions = {8.0f, 0, 3, 1, 0};
 
 // Copies the caller's options (NULL = defaults) into *out once, so the
 // launches of one call all see the same values; false if a field is out of
@@ -27,6 +27,7 @@ bool read_options(const fa_options *opts, fa_options *out) {
     if (o.poly_eighths < 0 || o.poly_eighths > 2) return false;
     if (o.poly_degree != 3 && o.poly_degree != 5) return false;
     if (o.longest_first != 0 && o.longest_first != 1) return false;
+    if (o.fused_backward != 0 && o.fused_backward != 1) return false;
     *out = o;
     return true;
 }
@@ -48,6 +49,32 @@ fa_status check_shape(int B, int H, int S, int d, bool *empty) {
 }
 
 bool good_scale(float s) { return isfinite(s) && s > 0.0f; }
+
+// Workspace layout of the backward: -D and LSE*log2 e (fp32 [BH][S] each),
+// then, 256-byte aligned, the sync words of the single-pass backward: 16
+// claim counters, an error word, padding to 32, and one turn flag per
+// (head, block of 32 queries, wave slice of 8).
+size_t sync_offset(int64_t bh, int64_t S) { return ((size_t)(8 * bh * S) + 255) / 256 * 256; }
+int64_t sync_words(int64_t bh, int64_t S) { return 32 + bh * ((S + 31) / 32) * 8; }
+
+// Compute units and XCDs of the current device, looked up once per device.
+constexpr int kMaxDev = 64;
+std::atomic<int> g_ncu[kMaxDev], g_nxcd[kMaxDev];
+
+void device_counts(int *ncu, int *nxcd) {
+    *ncu = *nxcd = 0;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return;
+    int c = g_ncu[dev].load(std::memory_order_relaxed), x = g_nxcd[dev].load(std::memory_order_relaxed);
+    if (c <= 0) {
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) c = 0;
+        if (hipDeviceGetAttribute(&x, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess) x = 0;
+        g_nxcd[dev].store(x, std::memory_order_relaxed);
+        g_ncu[dev].store(c, std::memory_order_relaxed);
+    }
+    *ncu = c;
+    *nxcd = x;
+}
 
 fa_status hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
@@ -76,8 +103,8 @@ const char *fa_status_string(fa_status s) {
         case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dimension must be 64 or 128";
         case FA_ERR_HIP: return "FA_ERR_HIP: kernel launch or device symbol lookup failed";
         case FA_ERR_TOO_LARGE:
-            return "FA_ERR_TOO_LARGE: the workspace (2*B*H*S*4 bytes) exceeds the static scratch array "
-                   "of fa_bwd_noalloc (FA_NOALLOC_SCRATCH_BYTES)";
+            return "FA_ERR_TOO_LARGE: the workspace (fa_bwd_workspace_bytes) exceeds the static scratch "
+                   "array of fa_bwd_noalloc (FA_NOALLOC_SCRATCH_BYTES)";
     }
     return "unknown fa_status";
 }
@@ -140,7 +167,8 @@ fa_status fa_fwd_varlen(const void *Q, const void *K, const void *V, void *O, fl
 size_t fa_bwd_workspace_bytes(int B, int H, int S, int d) {
     (void)d;
     if (B <= 0 || H <= 0 || S <= 0) return 0;
-    return 2 * (size_t)B * (size_t)H * (size_t)S * sizeof(float);
+    const int64_t bh = (int64_t)B * H;
+    return sync_offset(bh, S) + ((size_t)sync_words(bh, S) * 4 + 255) / 256 * 256;
 }
 
 static fa_status check_bwd_common(int B, int H, int S, int d, const void *workspace,
@@ -167,6 +195,8 @@ fa_status fa_bwd_preprocess(const void *O, const void *dO, const float *LSE, int
     a.BH = B * H;
     a.S = S;
     a.d = d;
+    a.sync = (int *)((char *)workspace + sync_offset(a.BH, S));
+    a.nsync = (int)sync_words(a.BH, S);
     return hip_status(fa::launch_bwd_preprocess(a, (hipStream_t)stream));
 }
 
@@ -196,6 +226,8 @@ static fa_status bwd_grad_args(const void *Q, const void *K, const void *V,
     a->scale = scale;
     a->causal = causal == 1;
     a->lpt = o.longest_first != 0;
+    a->sync = (int *)((char *)workspace + sync_offset(a->BH, S));
+    a->nsync = (int)sync_words(a->BH, S);
     return FA_OK;
 }
 
@@ -228,6 +260,35 @@ fa_status fa_bwd_dq(const void *Q, const void *K, const void *V, const void *dO,
     return hip_status(fa::launch_bwd_dq(a, (hipStream_t)stream));
 }
 
+// Whether the single-pass backward can run on the current device for B*H
+// heads: one work queue per XCD holding whole heads.  Fills the launch counts.
+static bool fused_supported(fa::BwdArgs *a) {
+    int ncu = 0, nxcd = 0;
+    device_counts(&ncu, &nxcd);
+    if (ncu <= 0 || nxcd <= 0 || nxcd > 16 || a->BH % nxcd != 0) return false;
+    a->n_cu = ncu;
+    a->nxcd = nxcd;
+    return true;
+}
+
+fa_status fa_bwd_fused(const void *Q, const void *K, const void *V, const void *dO, float *dQ, void *dK,
+                       void *dV, int B, int H, int S, int d, float scale, int causal, const void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    fa::BwdArgs a;
+    bool empty = false;
+    fa_status st = bwd_grad_args(Q, K, V, dO, B, H, S, d, scale, causal, nullptr, workspace,
+                                 workspace_bytes, &a, &empty);
+    if (st != FA_OK || empty) return st;
+    const void *outs[] = {dQ, dK, dV};
+    for (const void *p : outs)
+        if (!p || !aligned16(p)) return FA_ERR_INVALID;
+    if (!fused_supported(&a)) return FA_ERR_UNSUPPORTED;
+    a.dQ = dQ;
+    a.dK = dK;
+    a.dV = dV;
+    return hip_status(fa::launch_bwd_fused(a, (hipStream_t)stream));
+}
+
 fa_status fa_bwd_opt(const void *Q, const void *K, const void *V, const void *O, const float *LSE,
                      const void *dO, float *dQ, void *dK, void *dV, int B, int H, int S, int d,
                      float scale, int causal, const fa_options *opts, void *workspace,
@@ -244,6 +305,15 @@ fa_status fa_bwd_opt(const void *Q, const void *K, const void *V, const void *O,
         if (!p || !aligned16(p)) return FA_ERR_INVALID;
     st = fa_bwd_preprocess(O, dO, LSE, B, H, S, d, workspace, workspace_bytes, stream);
     if (st != FA_OK) return st;
+    // The single-pass backward needs one work queue per XCD holding whole
+    // heads (B*H a multiple of the XCD count) and runs its own longest-first
+    // order; otherwise, or when asked, the split dK/dV and dQ kernels run.
+    if (o.fused_backward && o.longest_first && fused_supported(&a)) {
+        a.dQ = dQ;
+        a.dK = dK;
+        a.dV = dV;
+        return hip_status(fa::launch_bwd_fused(a, (hipStream_t)stream));
+    }
     st = fa_bwd_dkdv(Q, K, V, dO, dK, dV, B, H, S, d, scale, causal, &o, workspace, workspace_bytes,
                      stream);
     if (st != FA_OK) return st;

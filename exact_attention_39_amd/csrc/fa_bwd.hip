@@ -45,6 +45,7 @@
 // Causal: key blocks only meet query blocks at or below the diagonal; both
 // kernels order workgroup ids so the longest blocks start first (LPT,
 // technical summary, results).
+#include <algorithm>
 #include <type_traits>
 
 #include "fa_common.h"
@@ -72,7 +73,12 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const uint16_t *__res
                                                            const uint16_t *__restrict__ dO,
                                                            const float *__restrict__ LSE,
                                                            float *__restrict__ Dvec,
-                                                           float *__restrict__ L2vec, int64_t rows) {
+                                                           float *__restrict__ L2vec, int64_t rows,
+                                                           int *__restrict__ sync, int64_t nsync) {
+    // the sync words of the fused backward start at zero (a kernel, not a
+    // memset, so that the sequence can be captured in a graph)
+    const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (gid < nsync) sync[gid] = 0;
     constexpr int LPR = D / 8;  // lanes per row, 8 elements each
     constexpr int RPB = kThreads / LPR;
     const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
@@ -498,9 +504,10 @@ template <int D>
 hipError_t launch_pre_d(const BwdArgs &a, hipStream_t st) {
     constexpr int RPB = kThreads / (D / 8);
     const int64_t rows = (int64_t)a.BH * a.S;
-    const dim3 grid((unsigned)((rows + RPB - 1) / RPB)), block(kThreads);
+    const int64_t blocks = std::max((rows + RPB - 1) / RPB, ((int64_t)a.nsync + kThreads - 1) / kThreads);
+    const dim3 grid((unsigned)blocks), block(kThreads);
     hipLaunchKernelGGL((bwd_pre_kernel<D>), grid, block, 0, st, (const uint16_t *)a.O,
-                       (const uint16_t *)a.dO, a.LSE, a.Dvec, a.Dvec + rows, rows);
+                       (const uint16_t *)a.dO, a.LSE, a.Dvec, a.Dvec + rows, rows, a.sync, (int64_t)a.nsync);
     return hipGetLastError();
 }
 

@@ -33,17 +33,22 @@ struct BwdArgs {
     const float *LSE;
     float *dQ;
     void *dK, *dV;
-    float *Dvec;  // workspace: D (BH*S floats), then LSE*log2(e) (BH*S floats)
+    float *Dvec;  // workspace: -D (BH*S floats), then LSE*log2(e) (BH*S floats)
+    int *sync = nullptr;  // workspace: sync words of the fused backward (zeroed by the preprocess)
+    int nsync = 0;        // their count
     int BH, S, d;
     float scale;
     bool causal;
     bool lpt;     // causal: longest blocks first
+    int n_cu = 0;   // fused backward: compute units (one persistent workgroup each)
+    int nxcd = 0;   // fused backward: XCDs (one work queue each)
 };
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t st);
 hipError_t launch_bwd_preprocess(const BwdArgs &a, hipStream_t st);
 hipError_t launch_bwd_dkdv(const BwdArgs &a, hipStream_t st);
 hipError_t launch_bwd_dq(const BwdArgs &a, hipStream_t st);
+hipError_t launch_bwd_fused(const BwdArgs &a, hipStream_t st);
 hipError_t launch_exp2_poly(const float *x, float *y, int64_t n, int degree, hipStream_t st);
 
 }  // namespace fa

@@ -21,9 +21,12 @@
  * idea of the gist.science explainer, section 3 of the German page), and
  * schedules causal tiles longest-first (the LPT causal scheduler of the
  * technical summary, "Belangrijkste Resultaten").  The backward recomputes P
- * tile by tile from the saved LSE (technical summary, methodology item 3);
- * unlike the pages, which add dQ with global atomics, dQ comes from its own
- * pass over query blocks, because fp32 atomics are slow on this GPU.
+ * tile by tile from the saved LSE (technical summary, methodology item 3).
+ * Unlike the pages, which add dQ with global atomics, the default backward
+ * computes dQ in its own pass over query blocks (fp32 atomics are slow on
+ * this GPU); a single-pass variant that adds every key block's share of dQ
+ * in a fixed order -- the pages' deterministic mode -- with plain
+ * read-modify-writes kept inside one XCD's L2 is available (fa_bwd_fused).
  *
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
@@ -33,7 +36,13 @@
  *   - Q, K, V, O, dO, dK, dV: bf16 (raw 16-bit patterns), contiguous
  *     row-major [B][H][S][d].  LSE: fp32 [B][H][S].  dQ: fp32 [B][H][S][d].
  *     The backward workspace holds -D (fp32 [B][H][S], D_i = sum_k dO_ik
- *     O_ik, kept negated) followed by LSE * log2(e) (fp32 [B][H][S]).
+ *     O_ik, kept negated), LSE * log2(e) (fp32 [B][H][S]) and, from byte
+ *     round_up(8*B*H*S, 256) on, the int32 sync words of the single-pass
+ *     backward: 16 work-queue counters, an error word (index 16: nonzero
+ *     after a call means a bounded wait expired and the gradients of that
+ *     call are invalid; it cannot happen unless the hardware stops making
+ *     progress), padding to 32, then one turn flag per (b*H + h, block of
+ *     32 queries, wave slice of 8).
  *   - Every pointer must be 16-byte aligned.
  *   - d must be 64 or 128.  S may be any value >= 0 (ragged tails are
  *     masked).  B, H >= 0.  B*H*S == 0 is a valid empty call that launches
@@ -63,7 +72,7 @@ extern "C" {
 typedef enum {
     FA_OK = 0,
     FA_ERR_INVALID = 1,     /* null/misaligned pointer, bad size, scale or flag */
-    FA_ERR_UNSUPPORTED = 2, /* head dimension other than 64 or 128 */
+    FA_ERR_UNSUPPORTED = 2, /* head dimension other than 64 or 128; fa_bwd_fused: B*H vs XCDs */
     FA_ERR_HIP = 3,         /* the HIP runtime refused a launch or a device symbol lookup */
     FA_ERR_TOO_LARGE = 4    /* fa_bwd_noalloc: the workspace would not fit its static array */
 } fa_status;
@@ -85,19 +94,26 @@ typedef enum {
  *   poly_degree: 3 or 5 (default 3).
  *   longest_first: causal block order.  1 (default): longest blocks first,
  *     the LPT order of the technical summary's results (forward and dQ
- *     kernel: last query blocks first; dK/dV kernel: first key blocks
- *     first).  0: shortest first, kept for measuring what the order is
- *     worth.  The result does not depend on it.
- * The forward reads all four fields, the gradient kernels longest_first.
+ *     kernel: last query blocks first; dK/dV kernel and single-pass
+ *     backward: first key blocks first).  0: shortest first, kept for
+ *     measuring what the order is worth; it selects the split backward.
+ *     The result does not depend on it beyond the rounding of dQ sums.
+ *   fused_backward: 0 (default): fa_bwd / fa_bwd_opt run the split
+ *     backward (fa_bwd_dkdv + fa_bwd_dq), the faster one on MI355X; 1: the
+ *     single-pass backward (fa_bwd_fused) when B*H is a multiple of the
+ *     GPU's XCD count (8 on MI355X), else the split one.  Both are bitwise
+ *     repeatable; they differ in the rounding of dQ, dK and dV.
+ * The forward reads the first four fields, the backward the last two.
  */
 typedef struct fa_options {
     float rescale_tau;
     int poly_eighths;
     int poly_degree;
     int longest_first;
+    int fused_backward;
 } fa_options;
 
-/* The defaults: {8.0f, 0, 3, 1}. */
+/* The defaults: {8.0f, 0, 3, 1, 0}. */
 fa_options fa_default_options(void);
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -142,19 +158,22 @@ fa_status fa_fwd_varlen(const void *Q, const void *K, const void *V, void *O, fl
                         const int *cu_seqlens, int nseq, int H, int total, int max_seqlen, int d,
                         float scale, int causal, const fa_options *opts, void *stream);
 
-/* Bytes of workspace fa_bwd needs: 2*B*H*S fp32 values (-D and LSE*log2 e). */
+/* Bytes of workspace fa_bwd needs: round_up(8*B*H*S, 256) for -D and LSE*log2 e,
+ * plus round_up(4*(32 + 8*B*H*ceil(S/32)), 256) for the sync words. */
 size_t fa_bwd_workspace_bytes(int B, int H, int S, int d);
 
 /*
  * Backward pass for the O and LSE that fa_fwd produced from the same Q, K,
  * V, scale and causal flag.  Writes dQ (fp32 [B][H][S][d]), dK and dV
- * (bf16 [B][H][S][d]); every element is written exactly once (no atomics),
- * so the result is bitwise reproducible.  workspace must hold at least
- * fa_bwd_workspace_bytes(B, H, S, d) bytes of device memory; its contents on
- * entry are ignored and on return are -D and LSE*log2(e).  Outputs must not
- * overlap inputs.
- * Equivalent to fa_bwd_preprocess, then fa_bwd_dkdv and fa_bwd_dq (the two
- * gradient kernels are independent of each other), with default options.
+ * (bf16 [B][H][S][d]) without atomics: dK, dV are written once, dQ is
+ * either written once (split backward) or summed over key blocks in a
+ * fixed order (single-pass backward), so the result is bitwise
+ * reproducible.  workspace must hold at least fa_bwd_workspace_bytes(B, H,
+ * S, d) bytes of device memory; its contents on entry are ignored.  Outputs
+ * must not overlap inputs.  Steps: fa_bwd_preprocess, then the single-pass
+ * kernel, or fa_bwd_dkdv and fa_bwd_dq (see fa_options.fused_backward), with
+ * default options.  Calls that share a workspace must be ordered (one
+ * stream).
  */
 fa_status fa_bwd(const void *Q, const void *K, const void *V, const void *O, const float *LSE,
                  const void *dO, float *dQ, void *dK, void *dV,
@@ -169,7 +188,7 @@ fa_status fa_bwd_opt(const void *Q, const void *K, const void *V, const void *O,
 
 /*
  * Step 1 of fa_bwd: -D_i = -sum_k dO_ik O_ik and LSE_i * log2(e), fp32, into
- * workspace.  Same argument rules as fa_bwd.
+ * workspace, and the sync words zeroed.  Same argument rules as fa_bwd.
  */
 fa_status fa_bwd_preprocess(const void *O, const void *dO, const float *LSE,
                             int B, int H, int S, int d,
@@ -196,20 +215,36 @@ fa_status fa_bwd_dq(const void *Q, const void *K, const void *V,
                     const void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Step 2 of fa_bwd's single-pass variant (methodology item 3 of the
+ * technical summary: one pass over key blocks, dQ added in a fixed order):
+ * recompute P from LSE tile by tile and write dK, dV and dQ.  Reads the -D
+ * and LSE*log2 e that fa_bwd_preprocess left in workspace on the same
+ * stream, and uses (and leaves nonzero) its sync words, which that step
+ * zeroes: run fa_bwd_preprocess before every call.  FA_ERR_UNSUPPORTED if
+ * B*H is not a multiple of the GPU's XCD count or the device cannot be
+ * queried.  Longest-first order always.
+ */
+fa_status fa_bwd_fused(const void *Q, const void *K, const void *V, const void *dO,
+                       float *dQ, void *dK, void *dV,
+                       int B, int H, int S, int d, float scale, int causal,
+                       const void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): fa_bwd
  * with its workspace taken from a static device array of the library,
  * FA_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU, held by each GPU the library
  * runs on until the process ends.  Same arguments and results as fa_bwd
  * (default options), minus the workspace; it allocates nothing.
- *   - Limit: fa_bwd_workspace_bytes(B, H, S, d) = 8*B*H*S bytes must not
- *     exceed FA_NOALLOC_SCRATCH_BYTES (B*H*S <= 2^21 rows), else
- *     FA_ERR_TOO_LARGE, reported before any HIP call.
+ *   - Limit: fa_bwd_workspace_bytes(B, H, S, d) (about 9 bytes per query
+ *     row: B*H*S up to about 1.86 million rows) must not exceed
+ *     FA_NOALLOC_SCRATCH_BYTES, else FA_ERR_TOO_LARGE, reported before any
+ *     HIP call.
  *   - The array's device address is looked up (hipGetSymbolAddress) on the
  *     first call on each device, with that device current; a failed lookup
  *     gives FA_ERR_HIP.
  *   - All calls on one GPU share its array, which keeps the last call's
- *     contents (-D and LSE*log2 e).  Calls that overlap on one GPU (on
+ *     contents (-D, LSE*log2 e, sync words).  Calls that overlap on one GPU (on
  *     different streams, or from several threads without ordering) race on
  *     it and give wrong gradients; order them on one stream.
  */

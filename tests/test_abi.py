@@ -76,41 +76,48 @@ def test_empty_calls_are_ok_without_gpu(lib):
 
 
 def test_backward_checks(lib):
-    assert lib.fa_bwd_workspace_bytes(2, 3, 100, 128) == 2 * 2 * 3 * 100 * 4
+    # -D and LSE*log2 e (8 bytes per row, rounded up to 256), then the sync words of the
+    # single-pass backward: 32 + 8 * B*H * ceil(S / 32) int32, rounded up to 256 bytes
+    def ws_bytes(bh, S):
+        return (8 * bh * S + 255) // 256 * 256 + ((32 + 8 * bh * -(-S // 32)) * 4 + 255) // 256 * 256
+    assert lib.fa_bwd_workspace_bytes(2, 3, 100, 128) == ws_bytes(6, 100) == 4864 + 1024
+    assert lib.fa_bwd_workspace_bytes(1, 16, 32768, 128) == ws_bytes(16, 32768)
+    assert lib.fa_bwd_workspace_bytes(1, 1, 128, 128) == 1280
     p9 = [A] * 9
-    # workspace too small (needs 2 * 128 floats)
-    assert lib.fa_bwd(*p9, 1, 1, 128, 128, ctypes.c_float(0.1), 0, A, 1020, NULL) == 1
+    # workspace too small (needs 1280 bytes)
+    assert lib.fa_bwd(*p9, 1, 1, 128, 128, ctypes.c_float(0.1), 0, A, 1276, NULL) == 1
     # null workspace
     assert lib.fa_bwd(*p9, 1, 1, 128, 128, ctypes.c_float(0.1), 0, NULL, 1024, NULL) == 1
     # misaligned dQ
     p = list(p9)
     p[6] = MIS
-    assert lib.fa_bwd(*p, 1, 1, 128, 128, ctypes.c_float(0.1), 0, A, 1024, NULL) == 1
-    assert lib.fa_bwd(*p9, 1, 1, 128, 64 + 1, ctypes.c_float(0.1), 0, A, 1024, NULL) == 2
-    assert lib.fa_bwd_dkdv(*([A] * 6), 1, 1, 128, 128, ctypes.c_float(0.1), 3, NULL, A, 1024, NULL) == 1
-    assert lib.fa_bwd_dkdv(*([A] * 5), MIS, 1, 1, 128, 128, ctypes.c_float(0.1), 0, NULL, A, 1024, NULL) == 1
-    assert lib.fa_bwd_dq(*([A] * 4), MIS, 1, 1, 128, 128, ctypes.c_float(0.1), 0, NULL, A, 1024, NULL) == 1
-    assert lib.fa_bwd_dq(*([A] * 5), 1, 1, 128, 128, ctypes.c_float(0.0), 0, NULL, A, 1024, NULL) == 1
-    assert lib.fa_bwd_preprocess(A, MIS, A, 1, 1, 128, 128, A, 1024, NULL) == 1
-    assert lib.fa_bwd_preprocess(A, A, NULL, 1, 1, 128, 128, A, 1024, NULL) == 1
+    assert lib.fa_bwd(*p, 1, 1, 128, 128, ctypes.c_float(0.1), 0, A, 1280, NULL) == 1
+    assert lib.fa_bwd(*p9, 1, 1, 128, 64 + 1, ctypes.c_float(0.1), 0, A, 1280, NULL) == 2
+    assert lib.fa_bwd_dkdv(*([A] * 6), 1, 1, 128, 128, ctypes.c_float(0.1), 3, NULL, A, 1280, NULL) == 1
+    assert lib.fa_bwd_dkdv(*([A] * 5), MIS, 1, 1, 128, 128, ctypes.c_float(0.1), 0, NULL, A, 1280, NULL) == 1
+    assert lib.fa_bwd_dq(*([A] * 4), MIS, 1, 1, 128, 128, ctypes.c_float(0.1), 0, NULL, A, 1280, NULL) == 1
+    assert lib.fa_bwd_dq(*([A] * 5), 1, 1, 128, 128, ctypes.c_float(0.0), 0, NULL, A, 1280, NULL) == 1
+    assert lib.fa_bwd_preprocess(A, MIS, A, 1, 1, 128, 128, A, 1280, NULL) == 1
+    assert lib.fa_bwd_preprocess(A, A, NULL, 1, 1, 128, 128, A, 1280, NULL) == 1
     assert lib.fa_bwd_preprocess(A, A, A, 1, 1, 128, 128, A, 4, NULL) == 1
 
 
 def test_default_options(lib):
     import exact_attention_39_amd as fa
     o = lib.fa_default_options()
-    assert (o.rescale_tau, o.poly_eighths, o.poly_degree, o.longest_first) == (8.0, 0, 3, 1)
+    assert (o.rescale_tau, o.poly_eighths, o.poly_degree, o.longest_first, o.fused_backward) == (8.0, 0, 3, 1, 0)
     assert repr(fa.default_options()) == repr(fa.Options())
 
 
-@pytest.mark.parametrize("fields", [(-1.0, 0, 3, 1), (float("nan"), 0, 3, 1), (65.0, 0, 3, 1),
-                                    (8.0, 3, 3, 1), (8.0, -1, 3, 1), (8.0, 1, 4, 1), (8.0, 0, 3, 2)])
+@pytest.mark.parametrize("fields", [(-1.0, 0, 3, 1, 1), (float("nan"), 0, 3, 1, 1), (65.0, 0, 3, 1, 1),
+                                    (8.0, 3, 3, 1, 1), (8.0, -1, 3, 1, 1), (8.0, 1, 4, 1, 1), (8.0, 0, 3, 2, 1),
+                                    (8.0, 0, 3, 1, 2), (8.0, 0, 3, 1, -1)])
 def test_options_out_of_range_are_rejected_by_every_entry_point(lib, fields):
     """Per-call options are validated on the host, before any HIP call: every
     entry point that takes them returns FA_ERR_INVALID for a bad field."""
     import exact_attention_39_amd as fa
     o = fa.Options()
-    o.rescale_tau, o.poly_eighths, o.poly_degree, o.longest_first = fields
+    o.rescale_tau, o.poly_eighths, o.poly_degree, o.longest_first, o.fused_backward = fields
     po = ctypes.byref(o)
     f = ctypes.c_float
     assert lib.fa_fwd_opt(A, A, A, A, A, 1, 1, 128, 128, f(0.1), 0, po, NULL) == 1
@@ -225,9 +232,10 @@ def test_noalloc_backward_host_checks(lib):
     import exact_attention_39_amd as fa
     f = ctypes.c_float
     p9 = [A] * 9
-    rows_max = fa.NOALLOC_SCRATCH_BYTES // 8           # 8 bytes of workspace per (b, h, query row)
-    assert rows_max == 1 << 21
-    assert lib.fa_bwd_noalloc(*p9, 1, 1, rows_max + 1, 128, f(0.1), 0, NULL) == 4
+    # about 9 bytes of workspace per (b, h, query row): the largest S for B = H = 1
+    S_max = max(S for S in range(1800000, 1900000, 32) if lib.fa_bwd_workspace_bytes(1, 1, S, 128) <= fa.NOALLOC_SCRATCH_BYTES)
+    assert lib.fa_bwd_workspace_bytes(1, 1, S_max + 32, 128) > fa.NOALLOC_SCRATCH_BYTES
+    assert lib.fa_bwd_noalloc(*p9, 1, 1, S_max + 32, 128, f(0.1), 0, NULL) == 4
     assert lib.fa_bwd_noalloc(*p9, 2, 16, 65537, 128, f(0.1), 1, NULL) == 4
     assert lib.fa_bwd_noalloc(*p9, 1, 1, 128, 96, f(0.1), 0, NULL) == 2
     assert lib.fa_bwd_noalloc(*p9, 1, 1, 128, 128, f(0.0), 0, NULL) == 1

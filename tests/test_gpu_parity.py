@@ -123,6 +123,76 @@ def test_small_forward_backward_full_tensors(fa, B, H, S, d, causal):
     check_grad(bf16_to_np64(dv), gv, "dV")
 
 
+# B*H a multiple of the XCD count (8): fa_bwd takes the single-pass backward
+FUSED_SMALL = [
+    (1, 8, 300, 128, False),
+    (1, 8, 300, 128, True),
+    (2, 4, 515, 64, True),
+    (2, 4, 515, 64, False),
+    (1, 8, 1, 128, True),
+    (1, 16, 33, 128, False),
+    (1, 8, 256, 128, True),
+    (1, 8, 257, 64, True),
+    (1, 8, 700, 128, False),
+]
+
+
+def sync_error_word(ws, B, H, S):
+    """The error word of the single-pass backward's sync area in the workspace."""
+    off = (8 * B * H * S + 255) // 256 * 256
+    return int(ws.view(torch.int32)[off // 4 + 16].item())
+
+
+@pytest.mark.parametrize("B,H,S,d,causal", FUSED_SMALL)
+def test_fused_backward_full_tensors(fa, B, H, S, d, causal):
+    """The single-pass backward (dQ summed over key blocks in turn) against
+    the oracle on whole tensors, several key blocks and ragged tails; the
+    split backward on the same inputs too, and the error word stays 0."""
+    say(f"[fused] B={B} H={H} S={S} d={d} causal={causal}")
+    shape = (B, H, S, d)
+    seed = 5000 + S * 7 + d + int(causal) + H
+    qb, kb, vb, db = (rand_bits(shape, seed + i) for i in range(4))
+    scale = 1.0 / np.sqrt(d)
+    q, k, v, o, lse = run_fwd(fa, qb, kb, vb, causal, scale)
+    do = to_dev(db)
+    Q, K, V, dO = (gen.bf16_bits_to_f64(x) for x in (qb, kb, vb, db))
+    gq, gk, gv = oracle.attention_backward(Q, K, V, dO, scale, causal)
+    ws = torch.empty(max(1, fa.fa_bwd_workspace_bytes(B, H, S, d) // 4), dtype=torch.float32, device="cuda")
+    for fused in (True, False):
+        dq = torch.empty((B, H, S, d), dtype=torch.float32, device="cuda")
+        dk, dv = torch.empty_like(q), torch.empty_like(q)
+        fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, scale, causal, ws, opts=fa.Options(fused_backward=fused))
+        torch.cuda.synchronize()
+        if fused:
+            assert sync_error_word(ws, B, H, S) == 0, "a turn wait of the single-pass backward expired"
+        what = "fused" if fused else "split"
+        check_grad(dq.cpu().numpy().astype(np.float64), gq, f"{what} dQ")
+        check_grad(bf16_to_np64(dk), gk, f"{what} dK")
+        check_grad(bf16_to_np64(dv), gv, f"{what} dV")
+
+
+def test_fused_backward_repeatable_and_matches_split(fa):
+    """Two single-pass runs agree bit for bit (fixed order of the dQ sums);
+    against the split backward the gradients agree to fp32/bf16 rounding."""
+    say("[fused] repeatability")
+    shape = (1, 16, 2500, 128)
+    qb, kb, vb, db = (rand_bits(shape, 8100 + i) for i in range(4))
+    scale = 1.0 / np.sqrt(128)
+    for causal in (False, True):
+        q, k, v, o, lse = run_fwd(fa, qb, kb, vb, causal, scale)
+        do = to_dev(db)
+        fused = fa.Options(fused_backward=True)
+        g1 = fa.backward(q, k, v, o, lse, do, causal=causal, scale=scale, opts=fused)
+        g2 = fa.backward(q, k, v, o, lse, do, causal=causal, scale=scale, opts=fused)
+        gs = fa.backward(q, k, v, o, lse, do, causal=causal, scale=scale)
+        torch.cuda.synchronize()
+        for a, b, c_, nm in zip(g1, g2, gs, ("dQ", "dK", "dV")):
+            assert torch.equal(a, b), f"{nm} of the single-pass backward differs between runs (causal={causal})"
+            a64, c64 = a.float().cpu().numpy(), c_.float().cpu().numpy()
+            rel = np.abs(a64 - c64).max() / np.abs(c64).max()
+            assert rel <= 2e-2, f"{nm}: single-pass vs split rel diff {rel:.3e} (causal={causal})"
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_hand_worked_examples(fa, d):
     """The hand-derived closed forms of tests/golden/hand_worked_examples.json,
@@ -326,33 +396,41 @@ WORKLOAD_BWD = [
 
 @pytest.mark.parametrize("name,causal", WORKLOAD_BWD)
 def test_workload_backward_sampled(fa, name, causal):
-    """Sampled dQ rows of every head (cheap for the oracle: S*d work per row)
-    and sampled dK/dV key rows of the first, a middle and the last head (each
-    needs the full softmax of its head)."""
+    """Both backward variants (split, single-pass) in the launch configuration
+    bench.py times: sampled dQ rows of every head (cheap for the oracle:
+    S*d work per row) and sampled dK/dV key rows of the first, a middle and
+    the last head (each needs the full softmax of its head)."""
     say(f"[workload bwd] {name} causal={causal}")
     w = gen.WORKLOADS[name]
     bits = workload_bits(name)
     scale = gen.default_scale(w["d"])
     q, k, v, o, lse = run_fwd(fa, bits["q"], bits["k"], bits["v"], causal, scale)
     do = to_dev(bits["do"])
-    dq, dk, dv = fa.backward(q, k, v, o, lse, do, causal=causal, scale=scale)
-    torch.cuda.synchronize()
     S, B, H = w["S"], w["B"], w["H"]
     rows = sample_rows(S)
     idx = torch.from_numpy(rows).cuda()
-    dq_rows = dq[:, :, idx].cpu().numpy().astype(np.float64)
+    cols = np.array(sorted({0, 1, 127, 128, S // 3, S // 2, S - 129, S - 128, S - 1}), dtype=np.int64)
+    cidx = torch.from_numpy(cols).cuda()
+    got = {}
+    for fused in (False, True):
+        dq, dk, dv = fa.backward(q, k, v, o, lse, do, causal=causal, scale=scale,
+                                 opts=fa.Options(fused_backward=fused))
+        torch.cuda.synchronize()
+        got[fused] = (dq[:, :, idx].cpu().numpy().astype(np.float64), bf16_to_np64(dk[:, :, cidx]),
+                      bf16_to_np64(dv[:, :, cidx]))
+        del dq, dk, dv
     for b in range(B):
         for h in range(H):
             Q, K, V, dO = (head_f64(bits[t], b, h) for t in ("q", "k", "v", "do"))
             gq = oracle.backward_dq_rows(Q, K, V, dO, rows, scale, causal)
-            check_grad(dq_rows[b, h], gq, f"{name} dQ rows head ({b},{h})")
-    cols = np.array(sorted({0, 1, 127, 128, S // 3, S // 2, S - 129, S - 128, S - 1}), dtype=np.int64)
-    cidx = torch.from_numpy(cols).cuda()
+            for fused in (False, True):
+                check_grad(got[fused][0][b, h], gq, f"{name} dQ rows head ({b},{h}) fused={fused}")
     for b, h in sorted({(0, 0), (B // 2, H // 2), (B - 1, H - 1)}):
         Q, K, V, dO = (head_f64(bits[t], b, h) for t in ("q", "k", "v", "do"))
         gk, gv = oracle.backward_dkdv_cols(Q, K, V, dO, cols, scale, causal)
-        check_grad(bf16_to_np64(dk[b, h, cidx]), gk, f"{name} dK cols head ({b},{h})")
-        check_grad(bf16_to_np64(dv[b, h, cidx]), gv, f"{name} dV cols head ({b},{h})")
+        for fused in (False, True):
+            check_grad(got[fused][1][b, h], gk, f"{name} dK cols head ({b},{h}) fused={fused}")
+            check_grad(got[fused][2][b, h], gv, f"{name} dV cols head ({b},{h}) fused={fused}")
 
 
 @pytest.mark.parametrize("B,H,S,d,causal", [(2, 3, 3000, 64, False), (2, 3, 3000, 64, True),

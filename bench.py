@@ -101,6 +101,7 @@ def _time(fn, reps=5):
     """Mean milliseconds of fn() over reps launches (events on the current stream)."""
     import torch
     fn()
+    _warm(fn, min_ms=50.0)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -203,6 +204,7 @@ def varlen_bench(fa, gen, args, name="prefill_varlen_h16_d128"):
     call = lambda: fa.fa_fwd_varlen(q, k, v, o, lse, cu, maxlen, scale, w["causal"], stream)
     for _ in range(args.warmup):
         call()
+    _warm(call)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -268,12 +270,32 @@ def gemm_ceiling_tflops():
     return None
 
 
+def _warm(fn, min_ms=300.0, max_calls=2000):
+    """Call fn() until at least min_ms of GPU time has passed (the clock of an
+    idle GPU takes a while to come up; a few calls of a sub-millisecond
+    kernel are not enough)."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 1
+    while True:
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        if e0.elapsed_time(e1) >= min_ms or n >= max_calls:
+            return
+        n = min(max_calls, n * 4)
+
+
 def _events_ms(fn, warmup=3, reps=20):
     """Per-call milliseconds of fn() (HIP events on the current stream around
-    each call) after `warmup` untimed calls: (median, min)."""
+    each call) after `warmup` untimed calls and at least 300 ms of warm-up:
+    (median, min)."""
     import torch
     for _ in range(warmup):
         fn()
+    _warm(fn)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for e0, e1 in evs:
@@ -333,7 +355,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=24576)
     ap.add_argument("--varlen", action="store_true",

@@ -75,14 +75,23 @@ __device__ __forceinline__ int wave_sum(int v) {
 // Work item (sequence, query block) g of a packed batch, in longest-first
 // order, or !valid past the last item.  The cost of an item is its number of
 // key tiles: qblk + 1 blocks' worth when causal, the whole sequence when
-// not.  Items are grouped by cost level, highest first (causal: level =
-// qblk, one item per sequence with more blocks; non-causal: level = blocks
-// of the sequence - 1, all blocks of each such sequence), and by sequence
-// index within a level.  So no early-exit workgroups sit between the
-// working ones, whatever the order of the sequences in the batch.  Every
-// wave computes this on its own from cu (no LDS, no barrier); the level is
-// found by bisection over F(c) = number of items at levels >= c.  Blocks of a
-// sequence past nqb (a sequence longer than max_seqlen) are not counted.
+// not.  Items are grouped into levels, highest first, so no early-exit
+// workgroups sit between the working ones whatever the order of the
+// sequences in the batch:
+//   * causal: the level of a sequence is floor(log2(its block count)); the
+//     sequences of a level follow in index order, each with all its blocks,
+//     highest first.  So the workgroups running together are mostly blocks
+//     of one sequence (and, heads innermost, of one head on one XCD), which
+//     read the same key/value tiles: one tile in L2 serves many of them.
+//     The longest blocks of the longest sequences start first and the last
+//     items are blocks of the shortest sequences, which keeps the tail
+//     short (the longest-first idea at the granularity of sequences);
+//   * non-causal: level = blocks of the sequence - 1 (all blocks of a
+//     sequence cost the same), all blocks of each such sequence in turn.
+// Every wave computes this on its own from cu (no LDS, no barrier); the
+// level is found by bisection over F(c) = number of items at levels >= c.
+// Blocks of a sequence past nqb (a sequence longer than max_seqlen) are not
+// counted.
 struct VarlenItem {
     int seq, qblk;
     bool valid;
@@ -99,19 +108,27 @@ __device__ VarlenItem varlen_item(const int *__restrict__ cu, int nseq, int tota
     };
     const int nb0 = nb_at(lane);  // the first 64 sequences, kept
     auto nb_chunk = [&](int s0) { return s0 == 0 ? nb0 : nb_at(s0 + lane); };
+    // items of one sequence at level c, and at levels >= c
+    auto level_of = [](int nb) { return 31 - __builtin_clz((unsigned)nb); };   // nb >= 1
+    auto at_level = [&](int nb, int c) -> int {
+        if constexpr (CAUSAL) return (nb > 0 && level_of(nb) == c) ? nb : 0;
+        return nb == c + 1 ? nb : 0;
+    };
+    auto from_level = [&](int nb, int c) -> int {
+        if constexpr (CAUSAL) return (nb > 0 && level_of(nb) >= c) ? nb : 0;
+        return nb > c ? nb : 0;
+    };
     auto F = [&](int c) -> int {
         int acc = 0;
-        for (int s0 = 0; s0 < nseq; s0 += 64) {
-            const int nb = nb_chunk(s0);
-            acc += wave_sum(CAUSAL ? max(0, nb - c) : (nb > c ? nb : 0));
-        }
+        for (int s0 = 0; s0 < nseq; s0 += 64) acc += wave_sum(from_level(nb_chunk(s0), c));
         return acc;
     };
     VarlenItem it{0, 0, false};
     const int items = F(0);
     if (g >= items) return it;
     if (!lpt) g = items - 1 - g;
-    int lo = 0, hi = nqb, f_hi = 0;  // F(lo) > g >= F(hi)
+    const int nlev = CAUSAL ? 32 - __builtin_clz((unsigned)max(nqb, 1)) : nqb;
+    int lo = 0, hi = nlev, f_hi = 0;  // F(lo) > g >= F(hi)
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         const int f = F(mid);
@@ -122,23 +139,28 @@ __device__ VarlenItem varlen_item(const int *__restrict__ cu, int nseq, int tota
             f_hi = f;
         }
     }
-    // item r of level lo: causal, the r-th sequence with more than lo
-    // blocks; otherwise block r % (lo + 1) of the r / (lo + 1)-th sequence
-    // with exactly lo + 1 blocks
-    const int r = g - f_hi;
-    int k = CAUSAL ? r : r / (lo + 1);
-    it.qblk = CAUSAL ? lo : r - k * (lo + 1);
+    // item r of level lo: the sequence holding it by a running count over
+    // the sequences in index order, then the block within that sequence
+    int r = g - f_hi;
     for (int s0 = 0; s0 < nseq; s0 += 64) {
-        const int nb = nb_chunk(s0);
-        uint64_t m = __builtin_amdgcn_ballot_w64(CAUSAL ? nb > lo : nb == lo + 1);
-        const int cnt = __builtin_popcountll(m);
-        if (k < cnt) {
-            for (int i = 0; i < k; ++i) m &= m - 1;
-            it.seq = s0 + __builtin_ctzll(m);
+        const int cnt = at_level(nb_chunk(s0), lo);
+        int incl = cnt;   // inclusive prefix over the lanes of this chunk
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(incl, off);
+            if (lane >= off) incl += y;
+        }
+        const uint64_t m = __builtin_amdgcn_ballot_w64(incl > r);
+        if (m != 0) {
+            const int ln = __builtin_ctzll(m);
+            const int c_ln = __shfl(cnt, ln), incl_ln = __shfl(incl, ln);
+            const int k = r - (incl_ln - c_ln);          // position within the sequence's items
+            it.seq = s0 + ln;
+            it.qblk = CAUSAL ? c_ln - 1 - k : k;
             it.valid = true;
             return it;
         }
-        k -= cnt;
+        r -= __shfl(incl, 63);
     }
     return it;  // not reached: F counted the item
 }

@@ -97,11 +97,13 @@ def cpu_baseline(bits, S, d, scale, rows_n=2048):
                       f"(the dQ-rows routine does 8*S*d of the 10*S*d, so the CPU figure is flattered)"}
 
 
-def _time(fn, reps=5):
-    """Mean milliseconds of fn() over reps launches (events on the current stream)."""
+def _time(fn, reps=5, warm_calls=10):
+    """Mean milliseconds of fn() over reps launches (events on the current
+    stream) after 1 + warm_calls untimed ones: a fixed number of launches per
+    call, so that counter runs can attribute dispatches to configurations."""
     import torch
-    fn()
-    _warm(fn, min_ms=50.0)
+    for _ in range(1 + warm_calls):
+        fn()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -115,8 +117,11 @@ def _time(fn, reps=5):
 def _sweep(configs, rounds=3):
     """Median launch time of each (key, launch) in configs, the
     configurations interleaved over `rounds` rounds so that clock and
-    warm-up drift do not favour any of them."""
+    warm-up drift do not favour any of them (after 300 ms of warm-up on the
+    first configuration)."""
     times = {}
+    print(f"[ablation] sweep of {len(configs)} configurations: {_warm(configs[0][1])} warm-up launches of the "
+          "first, then per round and configuration 16 launches", file=sys.stderr, flush=True)
     for _ in range(rounds):
         for key, fn in configs:
             times.setdefault(key, []).append(_time(fn))
@@ -273,18 +278,19 @@ def gemm_ceiling_tflops():
 def _warm(fn, min_ms=300.0, max_calls=2000):
     """Call fn() until at least min_ms of GPU time has passed (the clock of an
     idle GPU takes a while to come up; a few calls of a sub-millisecond
-    kernel are not enough)."""
+    kernel are not enough).  Returns the number of calls."""
     import torch
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    n = 1
+    n, calls = 1, 0
     while True:
         e0.record()
         for _ in range(n):
             fn()
         e1.record()
         torch.cuda.synchronize()
+        calls += n
         if e0.elapsed_time(e1) >= min_ms or n >= max_calls:
-            return
+            return calls
         n = min(max_calls, n * 4)
 
 

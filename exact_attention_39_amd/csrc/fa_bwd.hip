@@ -22,12 +22,11 @@
 //
 // dK/dV kernel: one workgroup = 8 waves = 256 key rows; each wave owns 32
 // keys and takes the two 32-row halves of every 64-row query block in turn,
-// two waves per SIMD overlapping MFMA with softmax work.  V of the block
-// stays in LDS (rows padded rather than swizzled, since V is only read by
-// rows), each wave's K rows sit in registers (loaded once), dK and dV
-// accumulate in registers; query blocks (Q, dO, LSE, D) stream through a
-// double-buffered LDS stage filled by direct memory-to-LDS copies, one
-// barrier per 64 queries x 256 keys.  Per wave and half block: S = Q K^T
+// two waves per SIMD overlapping MFMA with softmax work.  Each wave's K and
+// V rows sit in registers (loaded once: the B operands of S = Q K^T and
+// dP = dO V^T), dK and dV accumulate in registers; query blocks (Q, dO,
+// LSE, D) stream through a double-buffered LDS stage filled by direct
+// memory-to-LDS copies, one barrier per 64 queries x 256 keys.  Per wave and half block: S = Q K^T
 // and dP = dO V^T (keys on the lanes), P and dS in registers, dV += P^T dO
 // and dK += dS^T Q with P and dS fed straight from the accumulators and dO,
 // Q through transposing LDS reads.
@@ -118,13 +117,8 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
     constexpr int QTILE = kQPerIter * ROWB;
-    // V rows are padded by 16 bytes instead of swizzled: V is only read by
-    // rows, 16 consecutive rows at one chunk then start 4 banks apart, and
-    // the k-step becomes an immediate offset.
-    constexpr int VPITCH = ROWB + 16;
-    constexpr int VTILE = kKB * VPITCH;
     constexpr int LDB = 4 * kQPerIter * 4;
-    constexpr int SMEM = LDB + 4 * QTILE + VTILE;
+    constexpr int SMEM = LDB + 4 * QTILE;
 
     // The query-side stages come first, so that each of their reads is one
     // register (lane offset with the stage folded in, flipped once per
@@ -135,7 +129,6 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
     fa_lds_char *sLD = smem;                     // [2][LSE 64 | D 64] floats
     fa_lds_char *sQ0 = sLD + LDB;                // [2] Q tiles
     fa_lds_char *sO0 = sQ0 + 2 * QTILE;          // [2] dO tiles
-    fa_lds_char *sV = sO0 + 2 * QTILE;           // V rows of the block
 
     const int lane = threadIdx.x & 63, w = wave_id();
     const int h = lane >> 5, n = lane & 31;
@@ -153,29 +146,18 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
     const fa_rsrc rL = make_rsrc(L2vec + (size_t)bh * S, (uint32_t)S * 4);
     const fa_rsrc rD = make_rsrc(Dvec + (size_t)bh * S, (uint32_t)S * 4);
 
-    {
-        // V rows of the block into the padded tile, through registers (the
-        // memory-to-LDS copies write 1 KB contiguously)
-        const fa_rsrc rV = make_rsrc(V + head, head_bytes);
-        constexpr int CPT = kKB * NCH / (64 * NW);  // 16-byte chunks per thread
-        fa_u32x4 vt[CPT];
-#pragma unroll
-        for (int k = 0; k < CPT; ++k) {
-            const int idx = (int)threadIdx.x + k * 64 * NW;
-            vt[k] = buf_load16(rV, (uint32_t)(k0 + idx / NCH) * ROWB + (idx % NCH) * 16);
-        }
-#pragma unroll
-        for (int k = 0; k < CPT; ++k) {
-            const int idx = (int)threadIdx.x + k * 64 * NW;
-            lds_write16(sV, (idx / NCH) * VPITCH + (idx % NCH) * 16, vt[k]);
-        }
-    }
-    // this wave's K rows, the B operands of S = Q K^T, straight to registers
-    fa_u32x4 kreg[KS];
+    // this wave's K and V rows, the B operands of S = Q K^T and dP = dO V^T,
+    // straight to registers (with them in registers the LDS holds only the
+    // query-side stages, and each half block reads 8 KB less from it)
+    fa_u32x4 kreg[KS], vreg[KS];
     {
         const fa_rsrc rK = make_rsrc(K + head, head_bytes);
+        const fa_rsrc rV = make_rsrc(V + head, head_bytes);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kreg[ks] = buf_load16(rK, (uint32_t)kv * ROWB + (16 * ks + 8 * h) * 2);
+        for (int ks = 0; ks < KS; ++ks) {
+            kreg[ks] = buf_load16(rK, (uint32_t)kv * ROWB + (16 * ks + 8 * h) * 2);
+            vreg[ks] = buf_load16(rV, (uint32_t)kv * ROWB + (16 * ks + 8 * h) * 2);
+        }
     }
 
     fa_f32x16 dkacc[DB], dvacc[DB];
@@ -202,15 +184,13 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
     __syncthreads();
 
     // Lane-dependent LDS offsets within query half 0 (half 1 is 32 rows,
-    // a multiple of the swizzle period, further on) and of this wave's V rows
-    // (padded rows: k-step ks is 32 ks bytes further).  The swizzle XORs the
+    // a multiple of the swizzle period, further on).  The swizzle XORs the
     // chunk index, so the Q/dO offset of k-step ks is that of k-step 0 with
     // 2 ks XORed into the chunk bits.  The query-side offsets (< QTILE / 2)
     // carry the stage as bit QTILE, flipped after every iteration; the LSE/D
     // offset carries it as bit 2 * kQPerIter * 4.
     int troff[DB][2];
     int qoff = tile_off<NCH>(n, h * 16);
-    const int voff0 = (int)(sV - smem) + (32 * w + n) * VPITCH + h * 16;
     int ldoff = 16 * h;
     {
         const int L = lane & 15;
@@ -246,7 +226,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
         for (int ks = 0; ks < KS; ++ks) {
             const int qo = qb ^ (ks << 5);
             sacc = mfma32(lds_read16(sQ, qo), kreg[ks], sacc);
-            pacc = mfma32(lds_read16(sO, qo), lds_read16(smem, voff0 + 32 * ks), pacc);
+            pacc = mfma32(lds_read16(sO, qo), vreg[ks], pacc);
         }
         fa_u32x4 pf[2], dsf[2];
 #pragma unroll

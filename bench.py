@@ -363,6 +363,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stored-ds", action="store_true",
+                    help="skip the second timing of the step with the stored-dS backward")
     ap.add_argument("--cpu-rows", type=int, default=24576)
     ap.add_argument("--varlen", action="store_true",
                     help="time the packed variable-length prefill forward (fa_fwd_varlen) on the "
@@ -416,49 +418,57 @@ def main():
     lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
     dq = torch.empty((B, H, S, d), dtype=torch.float32, device="cuda")
     dk, dv = torch.empty_like(q), torch.empty_like(q)
-    ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, S, d) // 4, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
     parts = [("fwd", False), ("bwd_pre", False), ("bwd_dkdv", False), ("bwd_dq", False),
              ("fwd", True), ("bwd_pre", True), ("bwd_dkdv", True), ("bwd_dq", True)]
     NP = len(parts) // 2
-
-    def launch(kind, causal):
-        if kind == "fwd":
-            fa.fa_fwd(q, k, v, o, lse, scale, causal, stream)
-        elif kind == "bwd_pre":
-            fa.fa_bwd_preprocess(o, do, lse, ws, stream)
-        elif kind == "bwd_dkdv":
-            fa.fa_bwd_dkdv(q, k, v, do, dk, dv, scale, causal, ws, stream)
-        else:
-            fa.fa_bwd_dq(q, k, v, do, dq, scale, causal, ws, stream)
-
-    def step(events=None):
-        for i, (kind, causal) in enumerate(parts):
-            if events is not None:
-                events[i].record(stream)
-            launch(kind, causal)
-        if events is not None:
-            events[len(parts)].record(stream)
-
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(args.steps)]
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(evs[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-
-    part_ms = [float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
-               for i in range(len(parts))]
     step_flop = sum(flops(B, H, S, d, c, bwd) for c in (False, True) for bwd in (False, True))
+
+    def timed_steps(opts, tag):
+        """Warm-up, then args.steps timed steps of the whole path with these
+        backward options; (ms per step by the host clock, mean ms per part by
+        HIP events on the launch stream)."""
+        nbytes = max(fa.fa_bwd_workspace_bytes(B, H, S, d, c, opts) for c in (False, True))
+        ws = torch.empty((nbytes + 3) // 4, dtype=torch.float32, device="cuda")
+
+        def launch(kind, causal):
+            if kind == "fwd":
+                fa.fa_fwd(q, k, v, o, lse, scale, causal, stream)
+            elif kind == "bwd_pre":
+                fa.fa_bwd_preprocess(o, do, lse, ws, stream)
+            elif kind == "bwd_dkdv":
+                fa.fa_bwd_dkdv(q, k, v, do, dk, dv, scale, causal, ws, stream, opts)
+            else:
+                fa.fa_bwd_dq(q, k, v, do, dq, scale, causal, ws, stream, opts)
+
+        def step(events=None):
+            for i, (kind, causal) in enumerate(parts):
+                if events is not None:
+                    events[i].record(stream)
+                launch(kind, causal)
+            if events is not None:
+                events[len(parts)].record(stream)
+
+        print(f"[bench] {tag}: warmup {args.warmup}", file=sys.stderr, flush=True)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(args.steps)]
+        print(f"[bench] {tag}: timing {args.steps} steps", file=sys.stderr, flush=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            step(evs[s])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        part_ms = [float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
+                   for i in range(len(parts))]
+        del ws
+        torch.cuda.empty_cache()
+        return wall * 1e3 / args.steps, part_ms, nbytes
+
+    ms_step, part_ms, _ = timed_steps(None, "default backward")
     value = step_flop / (ms_step / 1e3) / 1e12
 
     detail = {}
@@ -516,6 +526,20 @@ def main():
         "parts": detail,
         "roofline": roof,
     }
+    if not args.no_stored_ds:
+        # the same step with the stored-dS backward (fa_options.stored_ds): dQ
+        # from the dS the dK/dV kernel wrote to the workspace, no recompute
+        ms2, part2, nbytes2 = timed_steps(fa.Options(stored_ds=True), "stored-dS backward")
+        alt = {"ms_per_step": round(ms2, 3), "value": round(step_flop / (ms2 / 1e3) / 1e12, 1),
+               "workspace_gib": round(nbytes2 / 2 ** 30, 2)}
+        for causal in (False, True):
+            i0 = NP if causal else 0
+            b_ms = part2[i0 + 1] + part2[i0 + 2] + part2[i0 + 3]
+            tf = flops(B, H, S, d, causal, True) / (b_ms / 1e3) / 1e12
+            alt[f"bwd_{'causal' if causal else 'noncausal'}"] = {
+                "ms": round(b_ms, 4), "tflops": round(tf, 1), "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+                "dkdv_ms": round(part2[i0 + 2], 4), "dq_ms": round(part2[i0 + 3], 4)}
+        out["stored_ds_step"] = alt
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle on a row sample)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(bits, S, d, scale, args.cpu_rows)

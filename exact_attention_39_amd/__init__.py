@@ -28,17 +28,18 @@ _lib = None
 class Options(ctypes.Structure):
     """Per-call tuning options (struct fa_options of include/fa.h)."""
     _fields_ = [("rescale_tau", ctypes.c_float), ("poly_eighths", ctypes.c_int),
-                ("poly_degree", ctypes.c_int), ("longest_first", ctypes.c_int), ("fused_backward", ctypes.c_int)]
+                ("poly_degree", ctypes.c_int), ("longest_first", ctypes.c_int), ("fused_backward", ctypes.c_int),
+                ("stored_ds", ctypes.c_int)]
 
     def __init__(self, rescale_tau: float = 8.0, poly_eighths: int = 0, poly_degree: int = 3,
-                 longest_first: bool = True, fused_backward: bool = False):
+                 longest_first: bool = True, fused_backward: bool = False, stored_ds: bool = False):
         super().__init__(float(rescale_tau), int(poly_eighths), int(poly_degree), int(bool(longest_first)),
-                         int(bool(fused_backward)))
+                         int(bool(fused_backward)), int(bool(stored_ds)))
 
     def __repr__(self):
         return (f"Options(rescale_tau={self.rescale_tau}, poly_eighths={self.poly_eighths}, "
                 f"poly_degree={self.poly_degree}, longest_first={bool(self.longest_first)}, "
-                f"fused_backward={bool(self.fused_backward)})")
+                f"fused_backward={bool(self.fused_backward)}, stored_ds={bool(self.stored_ds)})")
 
 
 class FaError(RuntimeError):
@@ -70,6 +71,8 @@ def load_library():
     lib.fa_fwd_varlen.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_bwd_workspace_bytes_opt.argtypes = [i, i, i, i, i, op]
+    lib.fa_bwd_workspace_bytes_opt.restype = sz
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_bwd.restype = i
     lib.fa_bwd_opt.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, op, vp, sz, vp]
@@ -174,8 +177,11 @@ def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, max_seqlen: int, scale: float, ca
                                         int(bool(causal)), _opts(opts), _stream(stream)), "fa_fwd_varlen")
 
 
-def fa_bwd_workspace_bytes(B: int, H: int, S: int, d: int) -> int:
-    return int(load_library().fa_bwd_workspace_bytes(B, H, S, d))
+def fa_bwd_workspace_bytes(B: int, H: int, S: int, d: int, causal: bool = False, opts=None) -> int:
+    """Workspace bytes of a backward with these options (None = defaults)."""
+    if opts is None:
+        return int(load_library().fa_bwd_workspace_bytes(B, H, S, d))
+    return int(load_library().fa_bwd_workspace_bytes_opt(B, H, S, d, int(bool(causal)), _opts(opts)))
 
 
 def _bwd_checks(q, k, v, o, lse, do, dq, dk, dv):
@@ -325,6 +331,7 @@ def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = No
         dq = torch.empty((B, H, S, d), dtype=torch.float32, device=q.device)
         dk = torch.empty_like(q)
         dv = torch.empty_like(q)
-        ws = torch.empty(max(1, fa_bwd_workspace_bytes(B, H, S, d) // 4), dtype=torch.float32, device=q.device)
+        ws_bytes = fa_bwd_workspace_bytes(B, H, S, d, causal, opts)
+        ws = torch.empty(max(1, (ws_bytes + 3) // 4), dtype=torch.float32, device=q.device)
     fa_bwd(q, k, v, o, lse, do, dq, dk, dv, scale, causal, ws, s, opts)
     return dq, dk, dv

@@ -16,7 +16,7 @@
 
 namespace {
 
-constexpr fa_options kDefaultOptions = {8.0f, 0, 3, 1, 0};
+constexpr fa_options kDefaultOptions = {8.0f, 0, 3, 1, 0, 0};
 
 // Copies the caller's options (NULL = defaults) into *out once, so the
 // launches of one call all see the same values; false if a field is out of
@@ -28,6 +28,8 @@ bool read_options(const fa_options *opts, fa_options *out) {
     if (o.poly_degree != 3 && o.poly_degree != 5) return false;
     if (o.longest_first != 0 && o.longest_first != 1) return false;
     if (o.fused_backward != 0 && o.fused_backward != 1) return false;
+    if (o.stored_ds != 0 && o.stored_ds != 1) return false;
+    if (o.fused_backward && o.stored_ds) return false;  // two different backward algorithms
     *out = o;
     return true;
 }
@@ -171,20 +173,28 @@ size_t fa_bwd_workspace_bytes(int B, int H, int S, int d) {
     return sync_offset(bh, S) + ((size_t)sync_words(bh, S) * 4 + 255) / 256 * 256;
 }
 
-static fa_status check_bwd_common(int B, int H, int S, int d, const void *workspace,
-                                  size_t workspace_bytes, bool *empty) {
+size_t fa_bwd_workspace_bytes_opt(int B, int H, int S, int d, int causal, const fa_options *opts) {
+    fa_options o;
+    if (!read_options(opts, &o)) return 0;
+    const size_t base = fa_bwd_workspace_bytes(B, H, S, d);
+    if (!o.stored_ds || base == 0) return base;
+    return base + (size_t)fa::bwd_ds_bytes(B * H, S, causal != 0);
+}
+
+static fa_status check_bwd_common(int B, int H, int S, int d, int causal, const fa_options &o,
+                                  const void *workspace, size_t workspace_bytes, bool *empty) {
     fa_status st = check_shape(B, H, S, d, empty);
     if (st != FA_OK) return st;
     if (*empty) return FA_OK;
     if (!workspace || !aligned16(workspace)) return FA_ERR_INVALID;
-    if (workspace_bytes < fa_bwd_workspace_bytes(B, H, S, d)) return FA_ERR_INVALID;
+    if (workspace_bytes < fa_bwd_workspace_bytes_opt(B, H, S, d, causal, &o)) return FA_ERR_INVALID;
     return FA_OK;
 }
 
 fa_status fa_bwd_preprocess(const void *O, const void *dO, const float *LSE, int B, int H, int S,
                             int d, void *workspace, size_t workspace_bytes, void *stream) {
     bool empty = false;
-    fa_status st = check_bwd_common(B, H, S, d, workspace, workspace_bytes, &empty);
+    fa_status st = check_bwd_common(B, H, S, d, 0, kDefaultOptions, workspace, workspace_bytes, &empty);
     if (st != FA_OK || empty) return st;
     if (!O || !dO || !LSE || !aligned16(O) || !aligned16(dO) || !aligned16(LSE)) return FA_ERR_INVALID;
     fa::BwdArgs a{};
@@ -207,9 +217,10 @@ static fa_status bwd_grad_args(const void *Q, const void *K, const void *V,
                                fa::BwdArgs *a, bool *empty) {
     fa_options o;
     if (!read_options(opts, &o)) return FA_ERR_INVALID;
-    fa_status st = check_bwd_common(B, H, S, d, workspace, workspace_bytes, empty);
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID;
+    fa_status st = check_bwd_common(B, H, S, d, causal, o, workspace, workspace_bytes, empty);
     if (st != FA_OK) return st;
-    if (!good_scale(scale) || (causal != 0 && causal != 1)) return FA_ERR_INVALID;
+    if (!good_scale(scale)) return FA_ERR_INVALID;
     if (*empty) return FA_OK;
     const void *ptrs[] = {Q, K, V, dO};
     for (const void *p : ptrs)
@@ -228,12 +239,14 @@ static fa_status bwd_grad_args(const void *Q, const void *K, const void *V,
     a->lpt = o.longest_first != 0;
     a->sync = (int *)((char *)workspace + sync_offset(a->BH, S));
     a->nsync = (int)sync_words(a->BH, S);
+    // the stored dS follows the base workspace (whose size is a multiple of 256)
+    if (o.stored_ds) a->dS = (char *)workspace + fa_bwd_workspace_bytes(B, H, S, d);
     return FA_OK;
 }
 
 fa_status fa_bwd_dkdv(const void *Q, const void *K, const void *V, const void *dO,
                       void *dK, void *dV, int B, int H, int S, int d, float scale, int causal,
-                      const fa_options *opts, const void *workspace, size_t workspace_bytes,
+                      const fa_options *opts, void *workspace, size_t workspace_bytes,
                       void *stream) {
     fa::BwdArgs a;
     bool empty = false;

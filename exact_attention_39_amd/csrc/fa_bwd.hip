@@ -41,6 +41,12 @@
 // In both kernels the dP accumulators start at -D (the workspace keeps D
 // negated), so they end as dP - D, and scale multiplies dK and dQ once in
 // the epilogues rather than every dS element.
+//
+// Stored dS (an option): the dK/dV kernel also writes its bf16 dS tiles to
+// the workspace (2 bytes per query-key pair the mask keeps) and a third
+// kernel computes dQ = scale * dS K from them: one contraction instead of
+// three, bound by reading dS back from HBM.  MI355X's 288 GB hold the
+// 32 GiB of one S = 32768, 16-head backward.
 // Causal: key blocks only meet query blocks at or below the diagonal; both
 // kernels order workgroup ids so the longest blocks start first (LPT,
 // technical summary, results).
@@ -100,17 +106,101 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const uint16_t *__res
     }
 }
 
+// ---------------------------------------------------------------- stored dS
+// Optionally dS travels from the dK/dV kernel to the dQ kernel through HBM
+// instead of being recomputed there (dQ = dS K then needs one product instead
+// of three): one 32 KB bf16 tile per (head, 256-key block kb, 64-query
+// iteration i), holding the dK/dV kernel's registers as they are (see the
+// store).  Causal: only the tiles i >= 4 kb that a key block visits exist,
+// packed block after block.
+constexpr int kDsTileBytes = 256 * 64 * 2;
+constexpr int kDsTileElems = kDsTileBytes / 2;
+// cache policy of the dS stores and loads: non-temporal (each line is read
+// once, by the next kernel, long after it has left L2)
+constexpr int kNonTemporal = 2;
+
+__host__ __device__ inline int64_t ds_tiles_per_head(int nkb, int nqi, bool causal) {
+    return causal ? (int64_t)nkb * nqi - 2 * (int64_t)nkb * (nkb - 1) : (int64_t)nkb * nqi;
+}
+
+__host__ __device__ inline int64_t ds_tile(int64_t bh, int kb, int i, int nkb, int nqi, bool causal) {
+    const int64_t head = bh * ds_tiles_per_head(nkb, nqi, causal);
+    if (causal) return head + (int64_t)kb * nqi - 2 * (int64_t)kb * (kb - 1) + (i - 4 * kb);
+    return head + (int64_t)kb * nqi + i;
+}
+
+// Copies issued from inline assembly (the stored-dS kernels).  After a copy
+// through the compiler's intrinsic, the first transposing LDS read waits for
+// every copy in flight, and so does the fence of __syncthreads: with copies
+// two tiles ahead, or with dS stores in flight that only the next kernel
+// reads, that wait would serialise them.  These kernels count their own
+// memory operations instead (s_waitcnt vmcnt counts a wave's loads and
+// stores in issue order) and their barriers carry no memory fence.
+typedef uint32_t fa_srd __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ fa_srd make_srd(const void *base, uint32_t num_bytes) {
+    const uint64_t p = (uint64_t)base;
+    fa_srd r;
+    r[0] = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32) & 0xffffu);
+    r[2] = __builtin_amdgcn_readfirstlane(num_bytes);
+    r[3] = 0x00020000u;
+    return r;
+}
+
+// buffer_load_dwordx4 / _dword ... lds: as buf_load_lds, invisible to the compiler.
+__device__ __forceinline__ void copy16_async(fa_srd r, fa_lds_char *lds_wave_base, uint32_t off) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(off), "s"(r)
+                 : "memory", "m0");
+}
+
+// The same with the non-temporal hint (data read once: the stored dS).
+__device__ __forceinline__ void copy16_async_nt(fa_srd r, fa_lds_char *lds_wave_base, uint32_t off) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                 :
+                 : "s"(m0), "v"(off), "s"(r)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ void copy4_async(fa_srd r, fa_lds_char *lds_wave_base, uint32_t off) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(off), "s"(r)
+                 : "memory", "m0");
+}
+
+// tile_to_lds through copy16_async.
+template <int NCH, int ROWS, int NW>
+__device__ __forceinline__ void tile_to_lds_async(fa_srd r, int row0, fa_lds_char *tile, int w, int lane) {
+    constexpr int ROWB = NCH * 16;
+    constexpr int INSTS = ROWS * ROWB / 1024;
+    static_assert(INSTS % NW == 0, "tile must split evenly over the waves");
+#pragma unroll
+    for (int k = 0; k < INSTS / NW; ++k) {
+        const int inst = w + NW * k;
+        const int row = inst * (1024 / ROWB) + lane / NCH;
+        const int c = (lane % NCH) ^ swz<NCH>(row);
+        copy16_async(r, tile + inst * 1024, (uint32_t)(row0 + row) * ROWB + c * 16);
+    }
+}
+
 // ---------------------------------------------------------------- dK, dV
 // 8 waves, 256 keys: wave w owns keys 32 w .. +31 of the block and takes the
 // two 32-row halves of every 64-row query block in turn.  (Against 128 keys
 // per workgroup with the query halves on the two waves of a SIMD: half the
 // barriers and stage copies per MFMA, and no dK/dV exchange at the end.)
 constexpr int kKB = 256;
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DSOUT>
 __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const float *__restrict__ L2vec, const float *__restrict__ Dvec, const uint16_t *__restrict__ dO,
-    uint16_t *__restrict__ dK, uint16_t *__restrict__ dV, int BH, int S, float scale, float c, int lpt) {
+    uint16_t *__restrict__ dK, uint16_t *__restrict__ dV, uint16_t *__restrict__ dS, int BH, int S,
+    float scale, float c, int lpt) {
     constexpr int NW = 8;
     constexpr int ROWB = D * 2;
     constexpr int NCH = ROWB / 16;
@@ -170,17 +260,33 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
     const int nqb = (S + kQPerIter - 1) / kQPerIter;
     const int ib = CAUSAL ? k0 / kQPerIter : 0;
 
+    [[maybe_unused]] const fa_srd aQ = make_srd(Q + head, head_bytes), adO = make_srd(dO + head, head_bytes);
+    [[maybe_unused]] const fa_srd aLD = make_srd(w == 0 ? (const void *)(L2vec + (size_t)bh * S)
+                                                         : (const void *)(Dvec + (size_t)bh * S),
+                                                 (uint32_t)S * 4);
     auto issue = [&](int i, int buf) {
-        tile_to_lds<NCH, kQPerIter, NW>(rQ, i * kQPerIter, sQ0 + buf * QTILE, w, lane);
-        tile_to_lds<NCH, kQPerIter, NW>(rdO, i * kQPerIter, sO0 + buf * QTILE, w, lane);
-        if (w < 2) {
-            fa_lds_char *dst = sLD + (buf * 2 + w) * kQPerIter * 4;
-            buf_load_lds<4>(w == 0 ? rL : rD, dst, (uint32_t)(i * kQPerIter + lane) * 4);
+        if constexpr (DSOUT) {
+            tile_to_lds_async<NCH, kQPerIter, NW>(aQ, i * kQPerIter, sQ0 + buf * QTILE, w, lane);
+            tile_to_lds_async<NCH, kQPerIter, NW>(adO, i * kQPerIter, sO0 + buf * QTILE, w, lane);
+            if (w < 2) copy4_async(aLD, sLD + (buf * 2 + w) * kQPerIter * 4, (uint32_t)(i * kQPerIter + lane) * 4);
+        } else {
+            tile_to_lds<NCH, kQPerIter, NW>(rQ, i * kQPerIter, sQ0 + buf * QTILE, w, lane);
+            tile_to_lds<NCH, kQPerIter, NW>(rdO, i * kQPerIter, sO0 + buf * QTILE, w, lane);
+            if (w < 2) {
+                fa_lds_char *dst = sLD + (buf * 2 + w) * kQPerIter * 4;
+                buf_load_lds<4>(w == 0 ? rL : rD, dst, (uint32_t)(i * kQPerIter + lane) * 4);
+            }
         }
     };
 
     if (ib < nqb) issue(ib, 0);
-    wait_vmem();
+    if constexpr (DSOUT) {
+        // the compiler's own wait (vmcnt(0)): it then knows the K and V rows
+        // have arrived and waits for nothing inside the loops
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+    } else {
+        wait_vmem();
+    }
     __syncthreads();
 
     // Lane-dependent LDS offsets within query half 0 (half 1 is 32 rows,
@@ -202,7 +308,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
                 troff[db][s2] = tile_off<NCH>(4 * h + 8 * s2 + (L >> 2), (32 * db + col) * 2);
     }
 
-    auto compute_half = [&](int q0, auto QHC, auto MASKC) {
+    auto compute_half = [&](int q0, fa_rsrc rds, auto QHC, auto MASKC) {
         constexpr int qh = decltype(QHC)::value;
         constexpr bool MASK = decltype(MASKC)::value;
         const fa_lds_char *sQ = sQ0 + qh * 32 * ROWB;
@@ -238,7 +344,12 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * g + e;
                 float pv = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, -l4[e]));
-                if constexpr (MASK) pv = kv > q0 + 32 * qh + qi + e ? 0.0f : pv;
+                if constexpr (MASK) {
+                    // keys past S only reach the stored dS: zero them there
+                    bool dead = DSOUT && kv >= S;
+                    if constexpr (CAUSAL) dead = dead || kv > q0 + 32 * qh + qi + e;
+                    pv = dead ? 0.0f : pv;
+                }
                 p[e] = pv;
                 ds[e] = pv * pacc[r];
             }
@@ -248,6 +359,17 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
             pf[t][wd + 1] = pack_bf16(p[2], p[3]);
             dsf[t][wd] = pack_bf16(ds[0], ds[1]);
             dsf[t][wd + 1] = pack_bf16(ds[2], ds[3]);
+        }
+        if constexpr (DSOUT) {
+            // The stored tile holds each lane's registers as they are: 16
+            // bytes (8 bf16 of key 32 w + n: queries 16 t + 4 h + 0..3, then
+            // 16 t + 8 + 4 h + 0..3 of query half qh) at byte
+            // ((2 qh + t) * 8 + w) * 1024 + lane * 16, so that every store
+            // instruction writes 1 KB of whole lines.
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                __builtin_amdgcn_raw_buffer_store_b128(dsf[t], rds, (uint32_t)(((2 * qh + t) * 8 + w) * 1024 + lane * 16),
+                                                       0, kNonTemporal);
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -268,9 +390,13 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
     auto step = [&](int i, auto MASKC) {
         const int buf = (i - ib) & 1;
         if (i + 1 < nqb) issue(i + 1, buf ^ 1);
-        compute_half(i * kQPerIter, std::integral_constant<int, 0>{}, MASKC);
+        // (without a stored dS: an empty resource, never used)
+        const fa_rsrc rds = DSOUT ? make_rsrc(dS + (size_t)ds_tile(bh, kblk, i, nkb, nqb, CAUSAL) * kDsTileElems,
+                                              kDsTileBytes)
+                                  : make_rsrc(dS, 0);
+        compute_half(i * kQPerIter, rds, std::integral_constant<int, 0>{}, MASKC);
         __builtin_amdgcn_sched_barrier(0);
-        compute_half(i * kQPerIter, std::integral_constant<int, 1>{}, MASKC);
+        compute_half(i * kQPerIter, rds, std::integral_constant<int, 1>{}, MASKC);
         // the next iteration reads the other stage
         qoff ^= QTILE;
         ldoff ^= 2 * kQPerIter * 4;
@@ -279,11 +405,20 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_kernel(
             troff[db][0] ^= QTILE;
             troff[db][1] ^= QTILE;
         }
-        wait_vmem();
-        __syncthreads();
+        if constexpr (DSOUT) {
+            // the copies for the next iteration are done once at most this
+            // iteration's four dS stores are in flight; no fence (the
+            // stores are read by another kernel)
+            asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        } else {
+            wait_vmem();
+            __syncthreads();
+        }
     };
 
-    const int i_plain = CAUSAL ? min(nqb, (k0 + kKB - 1) / kQPerIter + 1) : ib;
+    // masked iterations: the causal diagonal, and with a stored dS every
+    // iteration of a block that reaches past S
+    const int i_plain = (DSOUT && k0 + kKB > S) ? nqb : CAUSAL ? min(nqb, (k0 + kKB - 1) / kQPerIter + 1) : ib;
     for (int i = ib; i < i_plain; ++i) step(i, std::true_type{});
     for (int i = i_plain; i < nqb; ++i) step(i, std::false_type{});
 
@@ -480,6 +615,158 @@ __global__ __launch_bounds__(64 * kDqWaves<WIDE>, WIDE ? 1 : 2) void bwd_dq_kern
     }
 }
 
+// ---------------------------------------------------------------- dQ from stored dS
+// dQ = scale * dS K with dS read back from HBM (the dK/dV kernel stored it):
+// a GEMM with the keys as its long inner dimension, bound by the dS reads.
+// One workgroup = 8 waves = 256 queries (the four 64-query iterations
+// 4 qb .. 4 qb + 3 of the stored layout); wave w takes 32 queries, iteration
+// w / 2, half w % 2.  64-key tiles of K (swizzled rows) and of dS (four
+// 64-row x 128-byte chunks, one per iteration) stream through three LDS
+// stages, two tiles in flight.  Per wave and tile: dQ^T += K^T dS^T, both
+// operands by transposing reads: K^T as in the other kernels, dS^T from the
+// key rows of the stored tile (lane = query, 4 keys per read).
+constexpr int kDqDsStages = 3;
+
+// Copies of key tile kt into one stage: 2 (D = 128) or 1 (D = 64) for K and 4
+// for dS per wave, the count the waits below rely on.
+template <int D>
+__device__ __forceinline__ void dq_ds_issue(fa_srd rK, const uint16_t *dS, int bh, int kt, int qb,
+                                            int nkb, int nqi, bool causal, fa_lds_char *stage,
+                                            int w, int lane) {
+    constexpr int NCH = D / 8;
+    // K rows kt*64 .. +63 (rows past S arrive as zeros)
+    tile_to_lds_async<NCH, 64, 8>(rK, kt * 64, stage, w, lane);
+    // dS: chunk k = iteration 4 qb + k, key rows (kt % 4) * 64 .. +63 of the
+    // tile (kt / 4, 4 qb + k), into LDS rows of 128 bytes (one key, the 64
+    // queries in the stored unit order); wave w copies rows 8 w .. 8 w + 7
+    // of each chunk.  The 64-byte halves of a row swap on every other row
+    // pair so that the transposing reads (4 rows x 64 bytes per half wave)
+    // hit all 64 banks.  Unit u = 2 (2 qh + t) + h of key kk sits at byte
+    // ((2 qh + t) * 8 + kk / 32) * 1024 + (32 h + kk % 32) * 16 of the tile.
+    fa_lds_char *sds = stage + 64 * D * 2;
+    const int r = 8 * w + lane / 8, pc = lane % 8;
+    const int lc = pc ^ (((r >> 1) & 1) << 2);
+    const int kk = (kt & 3) * 64 + r;
+    const uint32_t goff = (uint32_t)((((lc >> 1) * 8 + (kk >> 5)) * 2 + (lc & 1)) * 512 + (kk & 31) * 16);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int i = 4 * qb + k;
+        // past the last iteration: an empty resource, the copy writes zeros
+        const bool live = i < nqi;
+        const int64_t tile = live ? ds_tile(bh, kt >> 2, i, nkb, nqi, causal) : 0;
+        copy16_async_nt(make_srd(dS + tile * kDsTileElems, live ? (uint32_t)kDsTileBytes : 0u),
+                        sds + k * 8192 + w * 1024, goff);
+    }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void bwd_dq_ds_kernel(const uint16_t *__restrict__ K,
+                                                           const uint16_t *__restrict__ dS,
+                                                           float *__restrict__ dQ, int BH, int S,
+                                                           float scale, int nqb, int lpt) {
+    constexpr int ROWB = D * 2;
+    constexpr int NCH = ROWB / 16;
+    constexpr int DB = D / 32;
+    constexpr int STAGE = 64 * ROWB + 4 * 8192;
+    __shared__ __attribute__((aligned(1024))) char smem_raw[kDqDsStages * STAGE];
+    fa_lds_char *smem = (fa_lds_char *)smem_raw;
+
+    const int lane = threadIdx.x & 63, w = wave_id();
+    const int h = lane >> 5, n = lane & 31;
+    const int bh = blockIdx.x % BH;
+    const int qi = blockIdx.x / BH;
+    const int qb = (CAUSAL && lpt) ? (nqb - 1 - qi) : qi;
+    const int q0 = qb * 256;
+    const int wq_lo = q0 + 32 * w;
+    const int nkb = (S + kKB - 1) / kKB, nqi = (S + kQPerIter - 1) / kQPerIter;
+    const int kv_end = CAUSAL ? min(S, q0 + 256) : S;
+    const int nkv = (kv_end + 63) / 64;
+    const size_t head = (size_t)bh * (size_t)S * D;
+    const fa_srd rK = make_srd(K + head, (uint32_t)S * ROWB);
+
+    fa_f32x16 dqacc[DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i) dqacc[i] = zero16();
+
+    // Lane offsets.  A (K^T, d rows): rows 16 ks + 8 h + 0..3 and + 4..7,
+    // columns 32 db + the lane's 16-column group.  B (dS^T, queries): the
+    // same key rows; in each 16-lane group (t = (lane >> 4) & 1), lane L
+    // points at key row L / 4 of the four and at the 8-byte run L % 4 =
+    // (hi, h_k) of unit (half, t, h_k): queries 16 t + 8 hi + 4 h_k + 0..3,
+    // so lane i of the group receives query 16 t + i, the lane's own column.
+    const int L = lane & 15, tq = (lane >> 4) & 1;
+    int aoff[DB][2], boff[2];
+    {
+        const int col = tq * 16 + (L & 3) * 4;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) aoff[db][s2] = tile_off<NCH>(8 * h + 4 * s2 + (L >> 2), (32 * db + col) * 2);
+        const int qh = w & 1, hk = L & 1, hi = (L >> 1) & 1;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const int row = 8 * h + 4 * s2 + (L >> 2);  // + 16 ks, which keeps (row >> 1) & 1
+            boff[s2] = 64 * ROWB + (w >> 1) * 8192 + row * 128 +
+                       (((qh ^ ((row >> 1) & 1)) << 6) | (tq << 5) | (hk << 4) | (hi << 3));
+        }
+    }
+
+    auto compute_tile = [&](const fa_lds_char *st) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const fa_u32x2 b0 = lds_read_tr(st + ks * 16 * 128, boff[0]);
+            const fa_u32x2 b1 = lds_read_tr(st + ks * 16 * 128, boff[1]);
+            const fa_u32x4 b = {b0[0], b0[1], b1[0], b1[1]};
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const fa_u32x2 a0 = lds_read_tr(st + ks * 16 * ROWB, aoff[db][0]);
+                const fa_u32x2 a1 = lds_read_tr(st + ks * 16 * ROWB, aoff[db][1]);
+                const fa_u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
+                dqacc[db] = mfma32(a, b, dqacc[db]);
+            }
+        }
+    };
+
+    const int npre = min(nkv, kDqDsStages - 1);
+    for (int j = 0; j < npre; ++j) dq_ds_issue<D>(rK, dS, bh, j, qb, nkb, nqi, CAUSAL, smem + j * STAGE, w, lane);
+    for (int j = 0; j < nkv; ++j) {
+        // tile j has landed (this wave's copies: the wait; everyone's: the
+        // barrier), and every wave is done with the stage tile j + 2 goes to
+        if (j + 1 < nkv) {
+            if constexpr (D == 128) asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        }
+        if (j + 2 < nkv)
+            dq_ds_issue<D>(rK, dS, bh, j + 2, qb, nkb, nqi, CAUSAL, smem + ((j + 2) % kDqDsStages) * STAGE, w, lane);
+        // causal: a key tile wholly above this wave's queries has dS = 0
+        if (!(CAUSAL && j * 64 > wq_lo + 31)) compute_tile(smem + (j % kDqDsStages) * STAGE);
+    }
+    __syncthreads();
+
+    // Epilogue as in the recomputing dQ kernel: scaled rows through LDS,
+    // whole-row 16-byte stores.
+    constexpr int RB4 = D * 4, NC4 = RB4 / 16;
+    fa_lds_char *sQd = smem + w * (32 * RB4);
+    auto off4 = [&](int row, int ch) { return row * RB4 + ((ch ^ (row & (NC4 - 1))) << 4); };
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            fa_u32x4 v = {__float_as_uint(dqacc[db][4 * g] * scale), __float_as_uint(dqacc[db][4 * g + 1] * scale),
+                          __float_as_uint(dqacc[db][4 * g + 2] * scale), __float_as_uint(dqacc[db][4 * g + 3] * scale)};
+            lds_write16(sQd, off4(n, 8 * db + 2 * g + h), v);
+        }
+    const fa_rsrc rdQ = make_rsrc(dQ + head, (uint32_t)S * D * 4);
+    constexpr int RPI = 1024 / RB4;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+        const int row = i * RPI + lane / NC4, ch = lane % NC4;
+        buf_store16(rdQ, (uint32_t)(wq_lo + row) * RB4 + ch * 16, lds_read16(sQd, off4(row, ch)));
+    }
+}
+
 template <int D>
 hipError_t launch_pre_d(const BwdArgs &a, hipStream_t st) {
     constexpr int RPB = kThreads / (D / 8);
@@ -491,14 +778,27 @@ hipError_t launch_pre_d(const BwdArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <int D, bool CAUSAL, bool DSOUT>
+hipError_t launch_dkdv_s(const BwdArgs &a, hipStream_t st) {
+    const int nkb = (a.S + kKB - 1) / kKB;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DSOUT>), dim3((unsigned)(a.BH * nkb)), dim3(2 * kThreads), 0,
+                       st, (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
+                       (const float *)a.Dvec + (size_t)a.BH * a.S, (const float *)a.Dvec,
+                       (const uint16_t *)a.dO, (uint16_t *)a.dK, (uint16_t *)a.dV, (uint16_t *)a.dS,
+                       a.BH, a.S, a.scale, a.scale * FA_LOG2E, (int)a.lpt);
+    return hipGetLastError();
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_dkdv_t(const BwdArgs &a, hipStream_t st) {
-    const int nkb = (a.S + kKB - 1) / kKB;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(a.BH * nkb)), dim3(2 * kThreads), 0, st,
-                       (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
-                       (const float *)a.Dvec + (size_t)a.BH * a.S, (const float *)a.Dvec,
-                       (const uint16_t *)a.dO, (uint16_t *)a.dK, (uint16_t *)a.dV,
-                       a.BH, a.S, a.scale, a.scale * FA_LOG2E, (int)a.lpt);
+    return a.dS ? launch_dkdv_s<D, CAUSAL, true>(a, st) : launch_dkdv_s<D, CAUSAL, false>(a, st);
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_dq_ds(const BwdArgs &a, hipStream_t st) {
+    const int nqb = (a.S + 255) / 256;
+    hipLaunchKernelGGL((bwd_dq_ds_kernel<D, CAUSAL>), dim3((unsigned)(a.BH * nqb)), dim3(512), 0, st,
+                       (const uint16_t *)a.K, (const uint16_t *)a.dS, a.dQ, a.BH, a.S, a.scale, nqb, (int)a.lpt);
     return hipGetLastError();
 }
 
@@ -515,6 +815,7 @@ hipError_t launch_dq_w(const BwdArgs &a, hipStream_t st) {
 
 template <int D, bool CAUSAL>
 hipError_t launch_dq_t(const BwdArgs &a, hipStream_t st) {
+    if (a.dS) return launch_dq_ds<D, CAUSAL>(a, st);
     // measured: the wide shape is 2 % faster non-causal from S = 8192 on,
     // even causal at S = 32768 and slower causal at S = 4096
     if constexpr (!CAUSAL) {
@@ -524,6 +825,11 @@ hipError_t launch_dq_t(const BwdArgs &a, hipStream_t st) {
 }
 
 }  // namespace
+
+int64_t bwd_ds_bytes(int BH, int S, bool causal) {
+    const int nkb = (S + kKB - 1) / kKB, nqi = (S + kQPerIter - 1) / kQPerIter;
+    return (int64_t)BH * ds_tiles_per_head(nkb, nqi, causal) * kDsTileBytes;
+}
 
 hipError_t launch_bwd_preprocess(const BwdArgs &a, hipStream_t st) {
     return a.d == 128 ? launch_pre_d<128>(a, st) : launch_pre_d<64>(a, st);

@@ -42,7 +42,11 @@ struct BwdArgs {
     bool lpt;     // causal: longest blocks first
     int n_cu = 0;   // fused backward: compute units (one persistent workgroup each)
     int nxcd = 0;   // fused backward: XCDs (one work queue each)
+    void *dS = nullptr;  // stored dS (bwd_ds_bytes): the dK/dV kernel writes it, the dQ kernel reads it
 };
+
+// Bytes of the stored dS of a backward over BH heads of length S.
+int64_t bwd_ds_bytes(int BH, int S, bool causal);
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t st);
 hipError_t launch_bwd_preprocess(const BwdArgs &a, hipStream_t st);

@@ -42,7 +42,9 @@
  *     after a call means a bounded wait expired and the gradients of that
  *     call are invalid; it cannot happen unless the hardware stops making
  *     progress), padding to 32, then one turn flag per (b*H + h, block of
- *     32 queries, wave slice of 8).
+ *     32 queries, wave slice of 8).  With fa_options.stored_ds the bf16 dS
+ *     tiles follow, from byte fa_bwd_workspace_bytes(B, H, S, d) on, in a
+ *     layout private to the library.
  *   - Every pointer must be 16-byte aligned.
  *   - d must be 64 or 128.  S may be any value >= 0 (ragged tails are
  *     masked).  B, H >= 0.  B*H*S == 0 is a valid empty call that launches
@@ -103,7 +105,16 @@ typedef enum {
  *     single-pass backward (fa_bwd_fused) when B*H is a multiple of the
  *     GPU's XCD count (8 on MI355X), else the split one.  Both are bitwise
  *     repeatable; they differ in the rounding of dQ, dK and dV.
- * The forward reads the first four fields, the backward the last two.
+ *   stored_ds: split backward only.  0 (default): the dQ kernel recomputes
+ *     S, dP and dS for itself (three matrix products per tile; workspace
+ *     O(B*H*S)).  1: the dK/dV kernel also writes its bf16 dS to the
+ *     workspace and the dQ kernel reads it back (one product per tile),
+ *     trading HBM capacity and traffic for two products: the workspace grows
+ *     by 2 bytes per (query, key) pair the mask keeps, about 2*B*H*S*S
+ *     (half that causal; fa_bwd_workspace_bytes_opt).  dK and dV are
+ *     bitwise the same either way, dQ differs in rounding.  Cannot be
+ *     combined with fused_backward (FA_ERR_INVALID).
+ * The forward reads the first four fields, the backward the last three.
  */
 typedef struct fa_options {
     float rescale_tau;
@@ -111,9 +122,10 @@ typedef struct fa_options {
     int poly_degree;
     int longest_first;
     int fused_backward;
+    int stored_ds;
 } fa_options;
 
-/* The defaults: {8.0f, 0, 3, 1, 0}. */
+/* The defaults: {8.0f, 0, 3, 1, 0, 0}. */
 fa_options fa_default_options(void);
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -162,6 +174,11 @@ fa_status fa_fwd_varlen(const void *Q, const void *K, const void *V, void *O, fl
  * plus round_up(4*(32 + 8*B*H*ceil(S/32)), 256) for the sync words. */
 size_t fa_bwd_workspace_bytes(int B, int H, int S, int d);
 
+/* Workspace bytes of fa_bwd_opt (and of its steps) with these options (NULL
+ * = defaults) and this causal flag; 0 for invalid options or an empty
+ * problem.  Equal to fa_bwd_workspace_bytes(B, H, S, d) unless stored_ds. */
+size_t fa_bwd_workspace_bytes_opt(int B, int H, int S, int d, int causal, const fa_options *opts);
+
 /*
  * Backward pass for the O and LSE that fa_fwd produced from the same Q, K,
  * V, scale and causal flag.  Writes dQ (fp32 [B][H][S][d]), dK and dV
@@ -169,7 +186,8 @@ size_t fa_bwd_workspace_bytes(int B, int H, int S, int d);
  * either written once (split backward) or summed over key blocks in a
  * fixed order (single-pass backward), so the result is bitwise
  * reproducible.  workspace must hold at least fa_bwd_workspace_bytes(B, H,
- * S, d) bytes of device memory; its contents on entry are ignored.  Outputs
+ * S, d) bytes of device memory (fa_bwd_opt: fa_bwd_workspace_bytes_opt with
+ * the same options and causal flag); its contents on entry are ignored.  Outputs
  * must not overlap inputs.  Steps: fa_bwd_preprocess, then the single-pass
  * kernel, or fa_bwd_dkdv and fa_bwd_dq (see fa_options.fused_backward), with
  * default options.  Calls that share a workspace must be ordered (one
@@ -197,17 +215,20 @@ fa_status fa_bwd_preprocess(const void *O, const void *dO, const float *LSE,
 /*
  * Step 2 of fa_bwd: recompute P from LSE tile by tile and write dK and dV
  * (one workgroup per block of 256 keys).  Reads the -D and LSE*log2(e) that
- * fa_bwd_preprocess left in workspace on the same stream.
+ * fa_bwd_preprocess left in workspace on the same stream; with stored_ds it
+ * also writes dS into workspace.
  */
 fa_status fa_bwd_dkdv(const void *Q, const void *K, const void *V,
                       const void *dO, void *dK, void *dV,
                       int B, int H, int S, int d, float scale, int causal, const fa_options *opts,
-                      const void *workspace, size_t workspace_bytes, void *stream);
+                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Step 3 of fa_bwd: recompute P and dP per block of 128 queries (256 for
  * non-causal S >= 8192) and write dQ = scale * dS K in fp32.  Reads the
- * workspace like fa_bwd_dkdv.
+ * workspace like fa_bwd_dkdv.  With stored_ds (the same options as step 2,
+ * on the same stream after it) it reads the dS that step 2 wrote instead,
+ * per block of 256 queries.
  */
 fa_status fa_bwd_dq(const void *Q, const void *K, const void *V,
                     const void *dO, float *dQ,

@@ -105,19 +105,23 @@ def test_backward_checks(lib):
 def test_default_options(lib):
     import exact_attention_39_amd as fa
     o = lib.fa_default_options()
-    assert (o.rescale_tau, o.poly_eighths, o.poly_degree, o.longest_first, o.fused_backward) == (8.0, 0, 3, 1, 0)
+    assert (o.rescale_tau, o.poly_eighths, o.poly_degree, o.longest_first, o.fused_backward,
+            o.stored_ds) == (8.0, 0, 3, 1, 0, 0)
+    assert ctypes.sizeof(fa.Options) == 24
     assert repr(fa.default_options()) == repr(fa.Options())
 
 
-@pytest.mark.parametrize("fields", [(-1.0, 0, 3, 1, 1), (float("nan"), 0, 3, 1, 1), (65.0, 0, 3, 1, 1),
-                                    (8.0, 3, 3, 1, 1), (8.0, -1, 3, 1, 1), (8.0, 1, 4, 1, 1), (8.0, 0, 3, 2, 1),
-                                    (8.0, 0, 3, 1, 2), (8.0, 0, 3, 1, -1)])
+@pytest.mark.parametrize("fields", [(-1.0, 0, 3, 1, 1, 0), (float("nan"), 0, 3, 1, 1, 0), (65.0, 0, 3, 1, 1, 0),
+                                    (8.0, 3, 3, 1, 1, 0), (8.0, -1, 3, 1, 1, 0), (8.0, 1, 4, 1, 1, 0),
+                                    (8.0, 0, 3, 2, 1, 0), (8.0, 0, 3, 1, 2, 0), (8.0, 0, 3, 1, -1, 0),
+                                    (8.0, 0, 3, 1, 0, 2), (8.0, 0, 3, 1, 0, -1),
+                                    (8.0, 0, 3, 1, 1, 1)])  # single-pass and stored dS exclude each other
 def test_options_out_of_range_are_rejected_by_every_entry_point(lib, fields):
     """Per-call options are validated on the host, before any HIP call: every
     entry point that takes them returns FA_ERR_INVALID for a bad field."""
     import exact_attention_39_amd as fa
     o = fa.Options()
-    o.rescale_tau, o.poly_eighths, o.poly_degree, o.longest_first, o.fused_backward = fields
+    o.rescale_tau, o.poly_eighths, o.poly_degree, o.longest_first, o.fused_backward, o.stored_ds = fields
     po = ctypes.byref(o)
     f = ctypes.c_float
     assert lib.fa_fwd_opt(A, A, A, A, A, 1, 1, 128, 128, f(0.1), 0, po, NULL) == 1
@@ -127,6 +131,40 @@ def test_options_out_of_range_are_rejected_by_every_entry_point(lib, fields):
     assert lib.fa_bwd_dq(*([A] * 5), 1, 1, 128, 128, f(0.1), 0, po, A, 1024, NULL) == 1
     # bad options are rejected even for empty calls (nothing else is looked at)
     assert lib.fa_fwd_opt(*([NULL] * 5), 1, 1, 0, 128, f(0.1), 0, po, NULL) == 1
+    assert lib.fa_bwd_workspace_bytes_opt(1, 1, 128, 128, 0, po) == 0
+
+
+def ds_tiles(S, causal):
+    """32 KB tiles of the stored dS per head: one per (256-key block, 64-query
+    iteration) that the mask keeps, causal: iterations i >= 4 kb."""
+    nkb, nqi = -(-S // 256), -(-S // 64)
+    return sum(nqi - (4 * kb if causal else 0) for kb in range(nkb))
+
+
+@pytest.mark.parametrize("B,H,S,d", [(1, 1, 1, 64), (2, 3, 100, 128), (1, 2, 300, 128), (1, 16, 32768, 128),
+                                     (2, 16, 16384, 128), (1, 4, 4099, 64)])
+def test_stored_ds_workspace(lib, B, H, S, d):
+    """With stored_ds the workspace is the default one plus the dS tiles;
+    a workspace of the default size is refused on the host by every step
+    that reads or writes dS."""
+    import exact_attention_39_amd as fa
+    f = ctypes.c_float
+    base = lib.fa_bwd_workspace_bytes(B, H, S, d)
+    on = fa.Options(stored_ds=True)
+    for causal in (0, 1):
+        assert lib.fa_bwd_workspace_bytes_opt(B, H, S, d, causal, NULL) == base
+        assert lib.fa_bwd_workspace_bytes_opt(B, H, S, d, causal, ctypes.byref(fa.Options())) == base
+        need = lib.fa_bwd_workspace_bytes_opt(B, H, S, d, causal, ctypes.byref(on))
+        assert need == base + B * H * ds_tiles(S, causal) * 32768
+        assert fa.fa_bwd_workspace_bytes(B, H, S, d, bool(causal), on) == need
+        po = ctypes.byref(on)
+        assert lib.fa_bwd_opt(*([A] * 9), B, H, S, d, f(0.1), causal, po, A, need - 16, NULL) == 1
+        assert lib.fa_bwd_dkdv(*([A] * 6), B, H, S, d, f(0.1), causal, po, A, base, NULL) == 1
+        assert lib.fa_bwd_dq(*([A] * 5), B, H, S, d, f(0.1), causal, po, A, base, NULL) == 1
+    # the causal layout keeps about half the tiles
+    if S >= 4096:
+        assert 0.49 < ds_tiles(S, True) / ds_tiles(S, False) < 0.52
+    assert lib.fa_bwd_workspace_bytes_opt(B, H, 0, d, 0, ctypes.byref(on)) == 0
 
 
 def test_options_are_read_once_per_call_no_shared_state(lib):

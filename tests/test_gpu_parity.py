@@ -115,12 +115,19 @@ def test_small_forward_backward_full_tensors(fa, B, H, S, d, causal):
     check_o(bf16_to_np64(o), o_ref, "fwd")
     check_lse(lse.cpu().numpy().astype(np.float64), lse_ref, "fwd")
     do = to_dev(db)
-    dq, dk, dv = fa.backward(q, k, v, o, lse, do, causal=causal, scale=scale)
-    torch.cuda.synchronize()
     gq, gk, gv = oracle.attention_backward(Q, K, V, dO, scale, causal)
-    check_grad(dq.cpu().numpy().astype(np.float64), gq, "dQ")
-    check_grad(bf16_to_np64(dk), gk, "dK")
-    check_grad(bf16_to_np64(dv), gv, "dV")
+    got = []
+    for stored in (False, True):
+        dq, dk, dv = fa.backward(q, k, v, o, lse, do, causal=causal, scale=scale,
+                                 opts=fa.Options(stored_ds=stored))
+        torch.cuda.synchronize()
+        what = "stored dS" if stored else "recomputed dS"
+        check_grad(dq.cpu().numpy().astype(np.float64), gq, f"{what} dQ")
+        check_grad(bf16_to_np64(dk), gk, f"{what} dK")
+        check_grad(bf16_to_np64(dv), gv, f"{what} dV")
+        got.append((dk, dv))
+    # the dK/dV kernel runs the same arithmetic whether or not it also stores dS
+    assert torch.equal(got[0][0], got[1][0]) and torch.equal(got[0][1], got[1][1])
 
 
 # B*H a multiple of the XCD count (8): fa_bwd takes the single-pass backward
@@ -394,12 +401,16 @@ WORKLOAD_BWD = [
 ]
 
 
+BWD_VARIANTS = {"split": dict(), "single-pass": dict(fused_backward=True), "stored dS": dict(stored_ds=True)}
+
+
 @pytest.mark.parametrize("name,causal", WORKLOAD_BWD)
 def test_workload_backward_sampled(fa, name, causal):
-    """Both backward variants (split, single-pass) in the launch configuration
-    bench.py times: sampled dQ rows of every head (cheap for the oracle:
-    S*d work per row) and sampled dK/dV key rows of the first, a middle and
-    the last head (each needs the full softmax of its head)."""
+    """The three backward variants (split with recomputed dS, single-pass,
+    split with stored dS) in the launch configuration bench.py times:
+    sampled dQ rows of every head (cheap for the oracle: S*d work per row)
+    and sampled dK/dV key rows of the first, a middle and the last head
+    (each needs the full softmax of its head)."""
     say(f"[workload bwd] {name} causal={causal}")
     w = gen.WORKLOADS[name]
     bits = workload_bits(name)
@@ -412,25 +423,26 @@ def test_workload_backward_sampled(fa, name, causal):
     cols = np.array(sorted({0, 1, 127, 128, S // 3, S // 2, S - 129, S - 128, S - 1}), dtype=np.int64)
     cidx = torch.from_numpy(cols).cuda()
     got = {}
-    for fused in (False, True):
-        dq, dk, dv = fa.backward(q, k, v, o, lse, do, causal=causal, scale=scale,
-                                 opts=fa.Options(fused_backward=fused))
+    for var, kw in BWD_VARIANTS.items():
+        say(f"[workload bwd]   {var}")
+        dq, dk, dv = fa.backward(q, k, v, o, lse, do, causal=causal, scale=scale, opts=fa.Options(**kw))
         torch.cuda.synchronize()
-        got[fused] = (dq[:, :, idx].cpu().numpy().astype(np.float64), bf16_to_np64(dk[:, :, cidx]),
-                      bf16_to_np64(dv[:, :, cidx]))
+        got[var] = (dq[:, :, idx].cpu().numpy().astype(np.float64), bf16_to_np64(dk[:, :, cidx]),
+                    bf16_to_np64(dv[:, :, cidx]))
         del dq, dk, dv
+        torch.cuda.empty_cache()  # the stored dS of the 32k workloads is 16-32 GiB
     for b in range(B):
         for h in range(H):
             Q, K, V, dO = (head_f64(bits[t], b, h) for t in ("q", "k", "v", "do"))
             gq = oracle.backward_dq_rows(Q, K, V, dO, rows, scale, causal)
-            for fused in (False, True):
-                check_grad(got[fused][0][b, h], gq, f"{name} dQ rows head ({b},{h}) fused={fused}")
+            for var in BWD_VARIANTS:
+                check_grad(got[var][0][b, h], gq, f"{name} dQ rows head ({b},{h}) {var}")
     for b, h in sorted({(0, 0), (B // 2, H // 2), (B - 1, H - 1)}):
         Q, K, V, dO = (head_f64(bits[t], b, h) for t in ("q", "k", "v", "do"))
         gk, gv = oracle.backward_dkdv_cols(Q, K, V, dO, cols, scale, causal)
-        for fused in (False, True):
-            check_grad(got[fused][1][b, h], gk, f"{name} dK cols head ({b},{h}) fused={fused}")
-            check_grad(got[fused][2][b, h], gv, f"{name} dV cols head ({b},{h}) fused={fused}")
+        for var in BWD_VARIANTS:
+            check_grad(got[var][1][b, h], gk, f"{name} dK cols head ({b},{h}) {var}")
+            check_grad(got[var][2][b, h], gv, f"{name} dV cols head ({b},{h}) {var}")
 
 
 @pytest.mark.parametrize("B,H,S,d,causal", [(2, 3, 3000, 64, False), (2, 3, 3000, 64, True),
@@ -446,7 +458,8 @@ def test_ragged_sampled(fa, B, H, S, d, causal):
     qb, kb, vb, dob = (rand_bits(shape, 7500 + i) for i in range(4))
     scale = 1.0 / np.sqrt(d)
     q, k, v, o, lse = run_fwd(fa, qb, kb, vb, causal, scale)
-    dq, dk, dv = fa.backward(q, k, v, o, lse, to_dev(dob), causal=causal, scale=scale)
+    grads = {st: fa.backward(q, k, v, o, lse, to_dev(dob), causal=causal, scale=scale,
+                             opts=fa.Options(stored_ds=st)) for st in (False, True)}
     torch.cuda.synchronize()
     rows = sample_rows(S)
     cols = np.array(sorted({0, 1, 127, 128, S // 3, S // 2, S - 129, S - 128, S - 1}), dtype=np.int64)
@@ -457,10 +470,12 @@ def test_ragged_sampled(fa, B, H, S, d, causal):
         check_o(bf16_to_np64(o[b, h, idx]), o_ref, f"d={d} O rows head ({b},{h})")
         check_lse(lse[b, h, idx].cpu().numpy().astype(np.float64), l_ref, f"d={d} LSE rows head ({b},{h})")
         gq = oracle.backward_dq_rows(Q, K, V, dO, rows, scale, causal)
-        check_grad(dq[b, h, idx].cpu().numpy().astype(np.float64), gq, f"d={d} dQ rows head ({b},{h})")
         gk, gv = oracle.backward_dkdv_cols(Q, K, V, dO, cols, scale, causal)
-        check_grad(bf16_to_np64(dk[b, h, cidx]), gk, f"d={d} dK cols head ({b},{h})")
-        check_grad(bf16_to_np64(dv[b, h, cidx]), gv, f"d={d} dV cols head ({b},{h})")
+        for st, (dq, dk, dv) in grads.items():
+            what = f"d={d} stored_ds={st}"
+            check_grad(dq[b, h, idx].cpu().numpy().astype(np.float64), gq, f"{what} dQ rows head ({b},{h})")
+            check_grad(bf16_to_np64(dk[b, h, cidx]), gk, f"{what} dK cols head ({b},{h})")
+            check_grad(bf16_to_np64(dv[b, h, cidx]), gv, f"{what} dV cols head ({b},{h})")
 
 
 def test_backward_is_bitwise_repeatable(fa):
@@ -472,11 +487,53 @@ def test_backward_is_bitwise_repeatable(fa):
     for causal in (False, True):
         q, k, v, o, lse = run_fwd(fa, qb, kb, vb, causal, scale)
         do = to_dev(db)
-        g1 = fa.backward(q, k, v, o, lse, do, causal=causal, scale=scale)
-        g2 = fa.backward(q, k, v, o, lse, do, causal=causal, scale=scale)
+        for stored in (False, True):
+            opts = fa.Options(stored_ds=stored)
+            g1 = fa.backward(q, k, v, o, lse, do, causal=causal, scale=scale, opts=opts)
+            g2 = fa.backward(q, k, v, o, lse, do, causal=causal, scale=scale, opts=opts)
+            torch.cuda.synchronize()
+            for a, b, nm in zip(g1, g2, ("dQ", "dK", "dV")):
+                assert torch.equal(a, b), f"{nm} differs between runs (causal={causal}, stored_ds={stored})"
+
+
+@pytest.mark.parametrize("B,H,S,d,causal", [(1, 3, 1100, 128, False), (2, 2, 1100, 128, True),
+                                             (1, 2, 777, 64, False), (1, 3, 2049, 64, True)])
+def test_stored_ds_steps_match_recompute(fa, B, H, S, d, causal):
+    """The stored-dS path through its C-ABI steps (preprocess, dK/dV writing
+    dS into the workspace, dQ reading it back) against the recomputing
+    steps on the same inputs: dK and dV bitwise equal, dQ equal to the
+    rounding of the bf16 dS (both compute dS = P (dP - D) from the same
+    inputs, in transposed orientations); and the dQ of the stored path
+    against the oracle on sampled rows."""
+    say(f"[stored dS steps] B={B} H={H} S={S} d={d} causal={causal}")
+    shape = (B, H, S, d)
+    qb, kb, vb, db = (rand_bits(shape, 9100 + S + i) for i in range(4))
+    scale = 1.0 / np.sqrt(d)
+    q, k, v, o, lse = run_fwd(fa, qb, kb, vb, causal, scale)
+    do = to_dev(db)
+    res = {}
+    for stored in (False, True):
+        opts = fa.Options(stored_ds=stored)
+        nb = fa.fa_bwd_workspace_bytes(B, H, S, d, causal, opts)
+        ws = torch.full(((nb + 3) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+        dq = torch.empty((B, H, S, d), dtype=torch.float32, device="cuda")
+        dk, dv = torch.empty_like(q), torch.empty_like(q)
+        fa.fa_bwd_preprocess(o, do, lse, ws)
+        fa.fa_bwd_dkdv(q, k, v, do, dk, dv, scale, causal, ws, opts=opts)
+        fa.fa_bwd_dq(q, k, v, do, dq, scale, causal, ws, opts=opts)
         torch.cuda.synchronize()
-        for a, b, nm in zip(g1, g2, ("dQ", "dK", "dV")):
-            assert torch.equal(a, b), f"{nm} differs between runs (causal={causal})"
+        res[stored] = (dq, dk, dv)
+    assert torch.equal(res[False][1], res[True][1]) and torch.equal(res[False][2], res[True][2])
+    a, b = res[False][0].double(), res[True][0].double()
+    assert torch.isfinite(b).all()
+    rel = float((a - b).abs().max() / a.abs().max())
+    assert rel <= 1e-3, f"dQ from stored dS vs recomputed: rel diff {rel:.3e}"
+    rows = sample_rows(S)
+    idx = torch.from_numpy(rows).cuda()
+    for bb, h in ((0, 0), (B - 1, H - 1)):
+        Q, K, V, dO = (gen.bf16_bits_to_f64(x[bb, h]) for x in (qb, kb, vb, db))
+        gq = oracle.backward_dq_rows(Q, K, V, dO, rows, scale, causal)
+        check_grad(res[True][0][bb, h, idx].cpu().numpy().astype(np.float64), gq, f"stored dS dQ head ({bb},{h})")
 
 
 def test_options_do_not_mix_across_threads(fa):
@@ -742,12 +799,13 @@ def test_causal_block_order_does_not_change_results(fa):
     shape = (1, 3, 700, 128)
     qb, kb, vb, db = (rand_bits(shape, 600 + i) for i in range(4))
     scale = 1.0 / np.sqrt(128)
-    out = []
-    for lpt in (True, False):
-        opts = fa.Options(longest_first=lpt)
-        q, k, v, o, lse = run_fwd(fa, qb, kb, vb, True, scale, opts)
-        g = fa.backward(q, k, v, o, lse, to_dev(db), causal=True, scale=scale, opts=opts)
-        torch.cuda.synchronize()
-        out.append((o, lse) + tuple(g))
-    for a, b, nm in zip(out[0], out[1], ("O", "LSE", "dQ", "dK", "dV")):
-        assert torch.equal(a, b), f"{nm} depends on the causal block order"
+    for stored in (False, True):
+        out = []
+        for lpt in (True, False):
+            opts = fa.Options(longest_first=lpt, stored_ds=stored)
+            q, k, v, o, lse = run_fwd(fa, qb, kb, vb, True, scale, opts)
+            g = fa.backward(q, k, v, o, lse, to_dev(db), causal=True, scale=scale, opts=opts)
+            torch.cuda.synchronize()
+            out.append((o, lse) + tuple(g))
+        for a, b, nm in zip(out[0], out[1], ("O", "LSE", "dQ", "dK", "dV")):
+            assert torch.equal(a, b), f"{nm} depends on the causal block order (stored_ds={stored})"

@@ -342,9 +342,15 @@ def configs_bench(fa, gen, args):
                 ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, S, d) // 4, dtype=torch.float32, device="cuda")
                 runs.append(("bwd", lambda: fa.fa_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], dq, dk, dv,
                                                       scale, causal, ws)))
+                # the same backward with the stored-dS option (its own, larger workspace)
+                on = fa.Options(stored_ds=True)
+                ws2 = torch.empty((fa.fa_bwd_workspace_bytes(B, H, S, d, causal, on) + 3) // 4,
+                                  dtype=torch.float32, device="cuda")
+                runs.append(("bwd_stored_ds", lambda: fa.fa_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], dq, dk,
+                                                                dv, scale, causal, ws2, opts=on)))
             for direction, fn in runs:
                 med, mn = _events_ms(fn)
-                fl = flops(B, H, S, d, causal, direction == "bwd")
+                fl = flops(B, H, S, d, causal, direction != "fwd")
                 tf = fl / (med / 1e3) / 1e12
                 print(json.dumps({
                     "metric": f"attention {direction} TFLOPS (median of 20 calls)", "value": round(tf, 1),
@@ -353,6 +359,8 @@ def configs_bench(fa, gen, args):
                     "config": {"workload": name, "B": B, "H": H, "S": S, "d": d, "causal": causal,
                                "boost": w["boost"]},
                 }), flush=True)
+            runs.clear()
+            torch.cuda.empty_cache()
         del t, o, lse
         torch.cuda.empty_cache()
 

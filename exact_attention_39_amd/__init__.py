@@ -322,7 +322,9 @@ def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = No
     """(dQ fp32, dK bf16, dV bf16) for the O, LSE that ``forward`` returned.
     Outputs and the workspace are allocated on the launch stream: the
     workspace returns to that stream's pool when this function returns, so
-    later allocations on it are ordered after the kernels that read it."""
+    later allocations on it are ordered after the kernels that read it.
+    With ``Options(stored_ds=True)`` the workspace also holds dS: about
+    2*B*H*S*S bytes (half that causal)."""
     import torch
     B, H, S, d = _dims(q)
     scale = d ** -0.5 if scale is None else scale

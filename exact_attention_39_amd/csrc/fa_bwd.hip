@@ -729,7 +729,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ds_kernel(const uint16_t *__res
 
     const int npre = min(nkv, kDqDsStages - 1);
     for (int j = 0; j < npre; ++j) dq_ds_issue<D>(rK, dS, bh, j, qb, nkb, nqi, CAUSAL, smem + j * STAGE, w, lane);
-    for (int j = 0; j < nkv; ++j) {
+    // one tile; the stage is a constant (the loop below is unrolled by the
+    // stage count), so every LDS read is a hoisted register plus an immediate
+    auto step = [&](int j, auto STC) {
+        constexpr int st = decltype(STC)::value;
         // tile j has landed (this wave's copies: the wait; everyone's: the
         // barrier), and every wave is done with the stage tile j + 2 goes to
         if (j + 1 < nkv) {
@@ -739,9 +742,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ds_kernel(const uint16_t *__res
             asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
         }
         if (j + 2 < nkv)
-            dq_ds_issue<D>(rK, dS, bh, j + 2, qb, nkb, nqi, CAUSAL, smem + ((j + 2) % kDqDsStages) * STAGE, w, lane);
+            dq_ds_issue<D>(rK, dS, bh, j + 2, qb, nkb, nqi, CAUSAL, smem + ((st + 2) % kDqDsStages) * STAGE, w, lane);
         // causal: a key tile wholly above this wave's queries has dS = 0
-        if (!(CAUSAL && j * 64 > wq_lo + 31)) compute_tile(smem + (j % kDqDsStages) * STAGE);
+        if (!(CAUSAL && j * 64 > wq_lo + 31)) compute_tile(smem + st * STAGE);
+    };
+    static_assert(kDqDsStages == 3, "the loop is unrolled by the stage count");
+    for (int j = 0; j < nkv; j += 3) {
+        step(j, std::integral_constant<int, 0>{});
+        if (j + 1 < nkv) step(j + 1, std::integral_constant<int, 1>{});
+        if (j + 2 < nkv) step(j + 2, std::integral_constant<int, 2>{});
     }
     __syncthreads();
 

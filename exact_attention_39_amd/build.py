@@ -19,6 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
+POISON_LIB = os.path.join(PKG, "libfa_poison.so")
 SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_bwd_fused.hip"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -31,8 +32,8 @@ FLAGS = [
 ]
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, extra, outdir: str = BUILD) -> str:
+    obj = os.path.join(outdir, os.path.splitext(src)[0] + ".o")
     cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -40,20 +41,31 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(extra_flags=(), verbose: bool = False) -> str:
-    """Compile every kernel source for gfx950 and link libfa.so.  Always
-    recompiles (this is the 'does it build' check)."""
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), SOURCES))
-    tmp = LIB + f".tmp{os.getpid()}"
+def _link(objs, lib: str) -> None:
+    tmp = lib + f".tmp{os.getpid()}"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(extra_flags=(), verbose: bool = False) -> str:
+    """Compile every kernel source for gfx950 and link libfa.so, and the
+    LDS-poison debug build libfa_poison.so (-DFA_LDS_POISON: every direct
+    LDS copy first fills its destination with NaN; the GPU tests compare its
+    outputs bit for bit with libfa.so).  Always recompiles (this is the
+    'does it build' check)."""
+    poison_dir = os.path.join(BUILD, "poison")
+    os.makedirs(poison_dir, exist_ok=True)
+    jobs = [(src, list(extra_flags), BUILD) for src in SOURCES]
+    jobs += [(src, list(extra_flags) + ["-DFA_LDS_POISON"], poison_dir) for src in SOURCES]
+    with cf.ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], POISON_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {POISON_LIB}")
     return LIB
 
 

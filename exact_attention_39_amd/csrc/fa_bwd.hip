@@ -150,6 +150,7 @@ __device__ __forceinline__ fa_srd make_srd(const void *base, uint32_t num_bytes)
 
 // buffer_load_dwordx4 / _dword ... lds: as buf_load_lds, invisible to the compiler.
 __device__ __forceinline__ void copy16_async(fa_srd r, fa_lds_char *lds_wave_base, uint32_t off) {
+    lds_poison(lds_wave_base, 16);
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
@@ -159,6 +160,7 @@ __device__ __forceinline__ void copy16_async(fa_srd r, fa_lds_char *lds_wave_bas
 
 // The same with the non-temporal hint (data read once: the stored dS).
 __device__ __forceinline__ void copy16_async_nt(fa_srd r, fa_lds_char *lds_wave_base, uint32_t off) {
+    lds_poison(lds_wave_base, 16);
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
                  :
@@ -167,6 +169,7 @@ __device__ __forceinline__ void copy16_async_nt(fa_srd r, fa_lds_char *lds_wave_
 }
 
 __device__ __forceinline__ void copy4_async(fa_srd r, fa_lds_char *lds_wave_base, uint32_t off) {
+    lds_poison(lds_wave_base, 4);
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                  :

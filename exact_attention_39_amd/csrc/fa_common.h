@@ -97,11 +97,35 @@ __device__ __forceinline__ void buf_atomic_add(fa_rsrc r, uint32_t off, float v)
     __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, off, 0, 0);
 }
 
+// LDS poison (debug build, -DFA_LDS_POISON): every direct copy first fills
+// its destination with all-ones bytes (NaN as fp32 and as bf16), waits for
+// that write, then copies.  A wave that reads a stage while another wave
+// refills it, or before its copy has landed, reads NaN instead of plausible
+// stale data, so a barrier out of place shows up as a changed result.
+// Nothing else differs: the arithmetic, and so every output bit, is that of
+// the normal build.
+__device__ __forceinline__ void lds_poison(fa_lds_char *lds_wave_base, int bytes) {
+#ifdef FA_LDS_POISON
+    fa_lds_char *p = lds_wave_base + (threadIdx.x & 63) * bytes;
+    if (bytes == 16) {
+        const fa_u32x4 ones = {~0u, ~0u, ~0u, ~0u};
+        *(__attribute__((address_space(3))) fa_u32x4 *)p = ones;
+    } else {
+        *(__attribute__((address_space(3))) uint32_t *)p = ~0u;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#else
+    (void)lds_wave_base;
+    (void)bytes;
+#endif
+}
+
 // Direct global -> LDS copy (buffer_load ... lds): every lane of the wave
 // fetches BYTES (4 or 16) at its own byte offset and the hardware stores them
 // at lds_wave_base + lane * BYTES.  lds_wave_base must be wave-uniform.
 template <int BYTES>
 __device__ __forceinline__ void buf_load_lds(fa_rsrc r, fa_lds_char *lds_wave_base, uint32_t off) {
+    lds_poison(lds_wave_base, BYTES);
     auto *dst = (__attribute__((address_space(3))) void *)lds_wave_base;
     if constexpr (BYTES == 16) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, off, 0, 0, 0);

@@ -37,6 +37,16 @@ def test_every_declared_symbol_is_exported(lib):
         assert getattr(lib, n) is not None
 
 
+def test_poison_build_exports_the_same_symbols():
+    """The LDS-poison debug build (libfa_poison.so) is the same library."""
+    path = os.path.join(ROOT, "exact_attention_39_amd", "libfa_poison.so")
+    if not os.path.exists(path):
+        pytest.fail("libfa_poison.so is not built: run __graft_entry__.build()")
+    nm = subprocess.check_output(["nm", "-D", "--defined-only", path], text=True)
+    exported = {l.split()[-1] for l in nm.splitlines() if " T " in l}
+    assert set(declared_functions()) <= exported
+
+
 def test_status_strings(lib):
     for code in range(5):
         assert lib.fa_status_string(code).decode().startswith("FA_")

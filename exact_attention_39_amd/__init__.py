@@ -73,6 +73,8 @@ def load_library():
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_bwd_workspace_bytes_opt.argtypes = [i, i, i, i, i, op]
     lib.fa_bwd_workspace_bytes_opt.restype = sz
+    lib.fa_bwd_workspace_bytes_min.argtypes = [i, i, i, i, i, op]
+    lib.fa_bwd_workspace_bytes_min.restype = sz
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_bwd.restype = i
     lib.fa_bwd_opt.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, op, vp, sz, vp]
@@ -182,6 +184,12 @@ def fa_bwd_workspace_bytes(B: int, H: int, S: int, d: int, causal: bool = False,
     if opts is None:
         return int(load_library().fa_bwd_workspace_bytes(B, H, S, d))
     return int(load_library().fa_bwd_workspace_bytes_opt(B, H, S, d, int(bool(causal)), _opts(opts)))
+
+
+def fa_bwd_workspace_bytes_min(B: int, H: int, S: int, d: int, causal: bool = False, opts=None) -> int:
+    """The least workspace fa_bwd accepts with these options (stored dS: one
+    head's dS; fa_bwd then takes the heads in groups)."""
+    return int(load_library().fa_bwd_workspace_bytes_min(B, H, S, d, int(bool(causal)), _opts(opts)))
 
 
 def _bwd_checks(q, k, v, o, lse, do, dq, dk, dv):

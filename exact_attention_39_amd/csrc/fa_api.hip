@@ -181,6 +181,14 @@ size_t fa_bwd_workspace_bytes_opt(int B, int H, int S, int d, int causal, const 
     return base + (size_t)fa::bwd_ds_bytes(B * H, S, causal != 0);
 }
 
+size_t fa_bwd_workspace_bytes_min(int B, int H, int S, int d, int causal, const fa_options *opts) {
+    fa_options o;
+    if (!read_options(opts, &o)) return 0;
+    const size_t base = fa_bwd_workspace_bytes(B, H, S, d);
+    if (!o.stored_ds || base == 0) return base;
+    return base + (size_t)fa::bwd_ds_bytes(1, S, causal != 0);
+}
+
 static fa_status check_bwd_common(int B, int H, int S, int d, int causal, const fa_options &o,
                                   const void *workspace, size_t workspace_bytes, bool *empty) {
     fa_status st = check_shape(B, H, S, d, empty);
@@ -202,6 +210,7 @@ fa_status fa_bwd_preprocess(const void *O, const void *dO, const float *LSE, int
     a.dO = dO;
     a.LSE = LSE;
     a.Dvec = (float *)workspace;
+    a.L2vec = a.Dvec + (size_t)B * H * S;
     a.BH = B * H;
     a.S = S;
     a.d = d;
@@ -231,6 +240,7 @@ static fa_status bwd_grad_args(const void *Q, const void *K, const void *V,
     a->V = V;
     a->dO = dO;
     a->Dvec = (float *)workspace;
+    a->L2vec = a->Dvec + (size_t)B * H * S;
     a->BH = B * H;
     a->S = S;
     a->d = d;
@@ -302,12 +312,51 @@ fa_status fa_bwd_fused(const void *Q, const void *K, const void *V, const void *
     return hip_status(fa::launch_bwd_fused(a, (hipStream_t)stream));
 }
 
+// The stored-dS backward in groups of heads that a smaller workspace holds:
+// each group runs the dK/dV kernel (writing its dS) and then the dQ kernel
+// on its own heads, reusing the same dS area.  Every head's arithmetic is
+// that of the single launch, so the result is bitwise the same.
+static fa_status bwd_stored_ds_groups(fa::BwdArgs a, int heads_per_group, hipStream_t stream) {
+    const int BH = a.BH;
+    const size_t rows = (size_t)a.S, elems = rows * a.d;
+    for (int h0 = 0; h0 < BH; h0 += heads_per_group) {
+        fa::BwdArgs g = a;
+        g.BH = std::min(heads_per_group, BH - h0);
+        g.Q = (const char *)a.Q + h0 * elems * 2;
+        g.K = (const char *)a.K + h0 * elems * 2;
+        g.V = (const char *)a.V + h0 * elems * 2;
+        g.dO = (const char *)a.dO + h0 * elems * 2;
+        g.dK = (char *)a.dK + h0 * elems * 2;
+        g.dV = (char *)a.dV + h0 * elems * 2;
+        g.dQ = a.dQ + h0 * elems;
+        g.Dvec = a.Dvec + h0 * rows;
+        g.L2vec = a.L2vec + h0 * rows;
+        fa_status st = hip_status(fa::launch_bwd_dkdv(g, stream));
+        if (st != FA_OK) return st;
+        st = hip_status(fa::launch_bwd_dq(g, stream));
+        if (st != FA_OK) return st;
+    }
+    return FA_OK;
+}
+
 fa_status fa_bwd_opt(const void *Q, const void *K, const void *V, const void *O, const float *LSE,
                      const void *dO, float *dQ, void *dK, void *dV, int B, int H, int S, int d,
                      float scale, int causal, const fa_options *opts, void *workspace,
                      size_t workspace_bytes, void *stream) {
     fa_options o;
     if (!read_options(opts, &o)) return FA_ERR_INVALID;
+    // Stored dS with a workspace too small for every head's dS at once, but
+    // large enough for at least one head's: run the heads in groups.
+    int group = 0;
+    if (o.stored_ds && causal >= 0 && causal <= 1) {
+        const size_t full = fa_bwd_workspace_bytes_opt(B, H, S, d, causal, &o);
+        const size_t base = fa_bwd_workspace_bytes(B, H, S, d);
+        const size_t per_head = base ? (size_t)fa::bwd_ds_bytes(1, S, causal != 0) : 0;
+        if (full && workspace_bytes < full && per_head && workspace_bytes >= base + per_head) {
+            group = (int)std::min<size_t>((workspace_bytes - base) / per_head, (size_t)B * H);
+            o.stored_ds = 0;  // so that the checks below ask only for the base workspace
+        }
+    }
     fa::BwdArgs a;
     bool empty = false;
     fa_status st = bwd_grad_args(Q, K, V, dO, B, H, S, d, scale, causal, &o, workspace,
@@ -318,6 +367,13 @@ fa_status fa_bwd_opt(const void *Q, const void *K, const void *V, const void *O,
         if (!p || !aligned16(p)) return FA_ERR_INVALID;
     st = fa_bwd_preprocess(O, dO, LSE, B, H, S, d, workspace, workspace_bytes, stream);
     if (st != FA_OK) return st;
+    if (group > 0) {
+        a.dQ = dQ;
+        a.dK = dK;
+        a.dV = dV;
+        a.dS = (char *)workspace + fa_bwd_workspace_bytes(B, H, S, d);
+        return bwd_stored_ds_groups(a, group, (hipStream_t)stream);
+    }
     // The single-pass backward needs one work queue per XCD holding whole
     // heads (B*H a multiple of the XCD count) and runs its own longest-first
     // order; otherwise, or when asked, the split dK/dV and dQ kernels run.

@@ -786,7 +786,7 @@ hipError_t launch_pre_d(const BwdArgs &a, hipStream_t st) {
     const int64_t blocks = std::max((rows + RPB - 1) / RPB, ((int64_t)a.nsync + kThreads - 1) / kThreads);
     const dim3 grid((unsigned)blocks), block(kThreads);
     hipLaunchKernelGGL((bwd_pre_kernel<D>), grid, block, 0, st, (const uint16_t *)a.O,
-                       (const uint16_t *)a.dO, a.LSE, a.Dvec, a.Dvec + rows, rows, a.sync, (int64_t)a.nsync);
+                       (const uint16_t *)a.dO, a.LSE, a.Dvec, a.L2vec, rows, a.sync, (int64_t)a.nsync);
     return hipGetLastError();
 }
 
@@ -795,7 +795,7 @@ hipError_t launch_dkdv_s(const BwdArgs &a, hipStream_t st) {
     const int nkb = (a.S + kKB - 1) / kKB;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DSOUT>), dim3((unsigned)(a.BH * nkb)), dim3(2 * kThreads), 0,
                        st, (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
-                       (const float *)a.Dvec + (size_t)a.BH * a.S, (const float *)a.Dvec,
+                       (const float *)a.L2vec, (const float *)a.Dvec,
                        (const uint16_t *)a.dO, (uint16_t *)a.dK, (uint16_t *)a.dV, (uint16_t *)a.dS,
                        a.BH, a.S, a.scale, a.scale * FA_LOG2E, (int)a.lpt);
     return hipGetLastError();
@@ -819,7 +819,7 @@ hipError_t launch_dq_w(const BwdArgs &a, hipStream_t st) {
     const int nqb = (a.S + kQPerBlock<WIDE> - 1) / kQPerBlock<WIDE>;
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, WIDE>), dim3((unsigned)(a.BH * nqb)), dim3(64 * kDqWaves<WIDE>), 0, st,
                        (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
-                       (const float *)a.Dvec + (size_t)a.BH * a.S, (const float *)a.Dvec,
+                       (const float *)a.L2vec, (const float *)a.Dvec,
                        (const uint16_t *)a.dO, a.dQ, a.BH, a.S, a.scale,
                        a.scale * FA_LOG2E, nqb, (int)a.lpt);
     return hipGetLastError();

@@ -418,7 +418,7 @@ template <int D, bool CAUSAL>
 hipError_t launch_fused_t(const BwdArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((bwd_fused_kernel<D, CAUSAL>), dim3((unsigned)a.n_cu), dim3(kFThreads), 0, st,
                        (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
-                       (const float *)a.Dvec + (size_t)a.BH * a.S, (const float *)a.Dvec,
+                       (const float *)a.L2vec, (const float *)a.Dvec,
                        (const uint16_t *)a.dO, a.dQ, (uint16_t *)a.dK, (uint16_t *)a.dV, a.sync, a.BH, a.S,
                        a.scale, a.scale * FA_LOG2E, a.nxcd);
     return hipGetLastError();

@@ -33,7 +33,8 @@ struct BwdArgs {
     const float *LSE;
     float *dQ;
     void *dK, *dV;
-    float *Dvec;  // workspace: -D (BH*S floats), then LSE*log2(e) (BH*S floats)
+    float *Dvec;           // workspace: -D (BH*S floats) ...
+    float *L2vec = nullptr;  // ... then LSE*log2(e) (BH*S floats)
     int *sync = nullptr;  // workspace: sync words of the fused backward (zeroed by the preprocess)
     int nsync = 0;        // their count
     int BH, S, d;

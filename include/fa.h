@@ -111,8 +111,10 @@ typedef enum {
  *     workspace and the dQ kernel reads it back (one product per tile),
  *     trading HBM capacity and traffic for two products: the workspace grows
  *     by 2 bytes per (query, key) pair the mask keeps, about 2*B*H*S*S
- *     (half that causal; fa_bwd_workspace_bytes_opt).  dK and dV are
- *     bitwise the same either way, dQ differs in rounding.  Cannot be
+ *     (half that causal; fa_bwd_workspace_bytes_opt), or with a smaller
+ *     workspace fa_bwd_opt takes the heads in groups (see
+ *     fa_bwd_workspace_bytes_min).  dK and dV are bitwise the same either
+ *     way, dQ differs in rounding.  Cannot be
  *     combined with fused_backward (FA_ERR_INVALID).
  * The forward reads the first four fields, the backward the last three.
  */
@@ -179,6 +181,14 @@ size_t fa_bwd_workspace_bytes(int B, int H, int S, int d);
  * problem.  Equal to fa_bwd_workspace_bytes(B, H, S, d) unless stored_ds. */
 size_t fa_bwd_workspace_bytes_opt(int B, int H, int S, int d, int causal, const fa_options *opts);
 
+/* The least workspace fa_bwd_opt accepts with these options: the same as
+ * fa_bwd_workspace_bytes_opt, except with stored_ds, where it is the
+ * default workspace plus the dS of one head.  Between this and
+ * fa_bwd_workspace_bytes_opt, fa_bwd_opt runs the heads in groups of as many
+ * as the workspace holds (dK/dV, then dQ, per group; bitwise the same
+ * result, more launches).  0 for invalid options or an empty problem. */
+size_t fa_bwd_workspace_bytes_min(int B, int H, int S, int d, int causal, const fa_options *opts);
+
 /*
  * Backward pass for the O and LSE that fa_fwd produced from the same Q, K,
  * V, scale and causal flag.  Writes dQ (fp32 [B][H][S][d]), dK and dV
@@ -186,7 +196,7 @@ size_t fa_bwd_workspace_bytes_opt(int B, int H, int S, int d, int causal, const 
  * either written once (split backward) or summed over key blocks in a
  * fixed order (single-pass backward), so the result is bitwise
  * reproducible.  workspace must hold at least fa_bwd_workspace_bytes(B, H,
- * S, d) bytes of device memory (fa_bwd_opt: fa_bwd_workspace_bytes_opt with
+ * S, d) bytes of device memory (fa_bwd_opt: fa_bwd_workspace_bytes_min with
  * the same options and causal flag); its contents on entry are ignored.  Outputs
  * must not overlap inputs.  Steps: fa_bwd_preprocess, then the single-pass
  * kernel, or fa_bwd_dkdv and fa_bwd_dq (see fa_options.fused_backward), with

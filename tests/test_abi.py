@@ -168,7 +168,10 @@ def test_stored_ds_workspace(lib, B, H, S, d):
         assert need == base + B * H * ds_tiles(S, causal) * 32768
         assert fa.fa_bwd_workspace_bytes(B, H, S, d, bool(causal), on) == need
         po = ctypes.byref(on)
-        assert lib.fa_bwd_opt(*([A] * 9), B, H, S, d, f(0.1), causal, po, A, need - 16, NULL) == 1
+        least = lib.fa_bwd_workspace_bytes_min(B, H, S, d, causal, po)
+        assert least == base + ds_tiles(S, causal) * 32768  # one head's dS: heads run in groups
+        assert lib.fa_bwd_workspace_bytes_min(B, H, S, d, causal, NULL) == base
+        assert lib.fa_bwd_opt(*([A] * 9), B, H, S, d, f(0.1), causal, po, A, least - 16, NULL) == 1
         assert lib.fa_bwd_dkdv(*([A] * 6), B, H, S, d, f(0.1), causal, po, A, base, NULL) == 1
         assert lib.fa_bwd_dq(*([A] * 5), B, H, S, d, f(0.1), causal, po, A, base, NULL) == 1
     # the causal layout keeps about half the tiles

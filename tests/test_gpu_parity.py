@@ -536,6 +536,41 @@ def test_stored_ds_steps_match_recompute(fa, B, H, S, d, causal):
         check_grad(res[True][0][bb, h, idx].cpu().numpy().astype(np.float64), gq, f"stored dS dQ head ({bb},{h})")
 
 
+@pytest.mark.parametrize("B,H,S,d,causal", [(2, 3, 777, 128, False), (2, 3, 777, 128, True),
+                                             (1, 5, 1000, 64, True)])
+def test_stored_ds_head_groups_are_bitwise_the_single_launch(fa, B, H, S, d, causal):
+    """With a workspace between fa_bwd_workspace_bytes_min and the full size,
+    fa_bwd runs the stored-dS backward in groups of heads (one head; four
+    heads); every head computes exactly as in the single launch."""
+    say(f"[stored dS groups] B={B} H={H} S={S} d={d} causal={causal}")
+    shape = (B, H, S, d)
+    qb, kb, vb, db = (rand_bits(shape, 9300 + S + i) for i in range(4))
+    scale = 1.0 / np.sqrt(d)
+    q, k, v, o, lse = run_fwd(fa, qb, kb, vb, causal, scale)
+    do = to_dev(db)
+    on = fa.Options(stored_ds=True)
+    full = fa.fa_bwd_workspace_bytes(B, H, S, d, causal, on)
+    least = fa.fa_bwd_workspace_bytes_min(B, H, S, d, causal, on)
+    base = fa.fa_bwd_workspace_bytes(B, H, S, d)
+    per_head = least - base
+    out = []
+    for nbytes in (full, least, base + 4 * per_head + 100):
+        ws = torch.full(((nbytes + 3) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+        dq = torch.empty((B, H, S, d), dtype=torch.float32, device="cuda")
+        dk, dv = torch.empty_like(q), torch.empty_like(q)
+        fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, scale, causal, ws, opts=on)
+        torch.cuda.synchronize()
+        out.append((dq, dk, dv))
+    for grouped in out[1:]:
+        for a, b, nm in zip(out[0], grouped, ("dQ", "dK", "dV")):
+            assert torch.equal(a, b), f"{nm}: head groups differ from the single launch"
+    Q, K, V, dO = (gen.bf16_bits_to_f64(x) for x in (qb, kb, vb, db))
+    gq, gk, gv = oracle.attention_backward(Q, K, V, dO, scale, causal)
+    check_grad(out[1][0].cpu().numpy().astype(np.float64), gq, "grouped stored dS dQ")
+    check_grad(bf16_to_np64(out[1][1]), gk, "grouped stored dS dK")
+    check_grad(bf16_to_np64(out[1][2]), gv, "grouped stored dS dV")
+
+
 def test_options_do_not_mix_across_threads(fa):
     """Options travel with each call.  Two host threads launch forwards with
     different options on their own streams at the same time; every result is

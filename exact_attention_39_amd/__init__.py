@@ -21,6 +21,9 @@ LIB_PATH = os.path.join(PKG, "libfa.so")
 
 FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_TOO_LARGE = 0, 1, 2, 3, 4
 NOALLOC_SCRATCH_BYTES = 16 << 20  # FA_NOALLOC_SCRATCH_BYTES of include/fa.h
+# backward(): most bytes of stored dS it allocates (8 GiB: four heads at S = 32768, which keeps
+# the speed of the single launch); beyond that the heads run in groups
+STORED_DS_WORKSPACE_CAP = 8 << 30
 
 _lib = None
 
@@ -332,7 +335,8 @@ def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = No
     workspace returns to that stream's pool when this function returns, so
     later allocations on it are ordered after the kernels that read it.
     With ``Options(stored_ds=True)`` the workspace also holds dS: about
-    2*B*H*S*S bytes (half that causal)."""
+    2*B*H*S*S bytes (half that causal), capped at STORED_DS_WORKSPACE_CAP
+    bytes (but at least one head's dS), beyond which the heads run in groups."""
     import torch
     B, H, S, d = _dims(q)
     scale = d ** -0.5 if scale is None else scale
@@ -342,6 +346,9 @@ def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = No
         dk = torch.empty_like(q)
         dv = torch.empty_like(q)
         ws_bytes = fa_bwd_workspace_bytes(B, H, S, d, causal, opts)
+        if opts is not None and opts.stored_ds:
+            ws_bytes = min(ws_bytes, max(fa_bwd_workspace_bytes_min(B, H, S, d, causal, opts),
+                                         fa_bwd_workspace_bytes(B, H, S, d) + STORED_DS_WORKSPACE_CAP))
         ws = torch.empty(max(1, (ws_bytes + 3) // 4), dtype=torch.float32, device=q.device)
     fa_bwd(q, k, v, o, lse, do, dq, dk, dv, scale, causal, ws, s, opts)
     return dq, dk, dv

@@ -315,13 +315,25 @@ fa_status fa_bwd_fused(const void *Q, const void *K, const void *V, const void *
 // The stored-dS backward in groups of heads that a smaller workspace holds:
 // each group runs the dK/dV kernel (writing its dS) and then the dQ kernel
 // on its own heads, reusing the same dS area.  Every head's arithmetic is
-// that of the single launch, so the result is bitwise the same.
-static fa_status bwd_stored_ds_groups(fa::BwdArgs a, int heads_per_group, hipStream_t stream) {
+// that of the single launch, so the result is bitwise the same.  Groups are
+// made of whole units of 8 heads (or of the largest power of two that fits,
+// below 8), so that a head's workgroups stay on the XCDs they use in the
+// single launch (head = workgroup id mod the group's head count), and the
+// units are spread evenly over as few groups as the workspace allows (a
+// small last group would leave most of the GPU idle, worst under the causal
+// mask, where one key block then sets the time).
+static fa_status bwd_stored_ds_groups(fa::BwdArgs a, int max_heads_per_group, hipStream_t stream) {
     const int BH = a.BH;
+    int unit = 1;
+    while (unit * 2 <= std::min(max_heads_per_group, 8)) unit *= 2;
+    const int units_per_group = max_heads_per_group / unit;
+    const int nunits = (BH + unit - 1) / unit;
+    const int ngroups = (nunits + units_per_group - 1) / units_per_group;
     const size_t rows = (size_t)a.S, elems = rows * a.d;
-    for (int h0 = 0; h0 < BH; h0 += heads_per_group) {
+    for (int gi = 0, h0 = 0; gi < ngroups; ++gi) {
         fa::BwdArgs g = a;
-        g.BH = std::min(heads_per_group, BH - h0);
+        const int units = nunits / ngroups + (gi < nunits % ngroups ? 1 : 0);
+        g.BH = std::min(units * unit, BH - h0);
         g.Q = (const char *)a.Q + h0 * elems * 2;
         g.K = (const char *)a.K + h0 * elems * 2;
         g.V = (const char *)a.V + h0 * elems * 2;
@@ -335,6 +347,7 @@ static fa_status bwd_stored_ds_groups(fa::BwdArgs a, int heads_per_group, hipStr
         if (st != FA_OK) return st;
         st = hip_status(fa::launch_bwd_dq(g, stream));
         if (st != FA_OK) return st;
+        h0 += g.BH;
     }
     return FA_OK;
 }

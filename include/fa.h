@@ -26,7 +26,10 @@
  * computes dQ in its own pass over query blocks (fp32 atomics are slow on
  * this GPU); a single-pass variant that adds every key block's share of dQ
  * in a fixed order -- the pages' deterministic mode -- with plain
- * read-modify-writes kept inside one XCD's L2 is available (fa_bwd_fused).
+ * read-modify-writes kept inside one XCD's L2 is available (fa_bwd_fused),
+ * and so is a dQ pass that reads the dS the dK/dV pass stored in the
+ * workspace instead of recomputing it (fa_options.stored_ds: O(S^2) bytes of
+ * workspace per head, traded for two of the dQ pass's three products).
  *
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller.  The library

@@ -12,7 +12,7 @@
  * "Probleemstelling") describe a faster implementation of the standard
  * attention of a Transformer that leaves the mathematical result unchanged.
  * The pages never print the formula, so this file writes out the standard
- * definition (the plainest reading; every reading is listed in the design doc):
+ * definition (the plainest reading of pages that state the method in words):
  *
  *   s_ij   = scale * sum_k q_ik k_jk
  *   A_i    = { j : j <= i } when causal (top-left aligned), else all j
